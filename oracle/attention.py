@@ -1,0 +1,222 @@
+"""Plain CPU oracle for on-the-fly block-sparse self-attention (Sol-Attn style).
+
+TEST INFRASTRUCTURE ONLY.  Nothing on the product path may import, call or
+execute this module: only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` use it.  It shares no code, table or
+helper with the HIP library and imports nothing from it.
+
+What it computes
+----------------
+The Sol-Attn project page ("Sol-Attn: Accelerating Video Generation Inference
+via On-the-Fly Attention Sparsification", nvlabs.github.io/Sana/Sol-Attn,
+section "Abstract") describes one online-softmax pass that (i) routes each
+query block to key blocks by a query-dependent threshold on a pooled score,
+(ii) computes exact attention over the selected blocks and (iii) adds an
+approximate correction for the long-tail mass of the skipped blocks by reusing
+below-threshold score columns.  The Sol-Engine README (raw README of
+NVlabs/Sana, branch sol-engine, section "Sol-Attention") adds that the
+replaced operator is video-token self-attention computed only on the most
+relevant key blocks, plus a light-weight compensating operation.
+
+The pages give no formula, so this module fixes the plainest concrete reading
+(every reading is listed in the design notes of the repository):
+
+* tokens are split into blocks of ``block`` consecutive tokens; block J holds
+  tokens [block*J, min(block*J + block, N)) and n_J is its actual size;
+* the pooled score ("proxy") is p_IJ = s * mean(q over I) . mean(k over J),
+  with s the softmax scale (1/sqrt(D) unless given);
+* block J is kept for query block I iff p_IJ >= max_J' p_IJ' - tau
+  (inclusive; tau = +inf keeps every block);
+* each skipped block J is modelled as n_J copies of its mean key and mean
+  value: row i sees the correction logit c_iJ = s * q_i . mean(k over J)
+  with multiplicity n_J -- c_iJ is the (i, J) entry of s * Q_I Kbar^T, the
+  "score column" of block J;
+* the output is the softmax over the union of exact logits (kept blocks) and
+  correction logits (skipped blocks, if correction is on), with natural-log
+  LSE lse_i = M_i + ln Z_i.
+
+It is evaluated here as the two-pass definition above in float64, not as an
+online softmax: first every logit of a row, then its max, then the sums.
+Each function below says which step it is.
+
+Pinned by tests/test_oracle_pins.py (closed forms of hand-derived cases,
+pure-Python brute force, library special cases, invariants).  Parity
+unpinned: none.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+__all__ = [
+    "block_ranges",
+    "block_means",
+    "default_scale",
+    "proxy_scores",
+    "route",
+    "attend_rows",
+    "forward_head",
+    "forward",
+    "dense_head",
+]
+
+
+def default_scale(D: int, scale: float | None = None) -> float:
+    """Softmax scale: 1/sqrt(D) unless an explicit positive scale is given.
+
+    The usual scaled-dot-product attention convention; the Sol-Engine README
+    (section "Sol-Attention") presents the sparse kernel as a drop-in for the
+    model's dense self-attention, which uses this scale.
+    """
+    if scale is not None and scale > 0:
+        return float(scale)
+    return 1.0 / math.sqrt(D)
+
+
+def block_ranges(N: int, block: int) -> list[tuple[int, int]]:
+    """Token ranges of the blocks: 64 consecutive tokens each (the last one ragged).
+
+    Blocks follow the given token order (frame-major raster of the video token
+    grid); no 3-D tiling or reordering is applied.
+    """
+    if block <= 0:
+        raise ValueError("block must be positive")
+    return [(s, min(s + block, N)) for s in range(0, N, block)]
+
+
+def block_means(x: np.ndarray, block: int) -> np.ndarray:
+    """Mean of each block's rows over the block's actual token count.
+
+    Step "pooled score" of the Sol-Attn Abstract, read as block means.
+    x: [N, D] float64 -> [Nb, D] float64.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    N = x.shape[0]
+    out = np.empty((len(block_ranges(N, block)), x.shape[1]), dtype=np.float64)
+    for J, (s, e) in enumerate(block_ranges(N, block)):
+        out[J] = x[s:e].sum(axis=0) / (e - s)
+    return out
+
+
+def proxy_scores(q: np.ndarray, k: np.ndarray, block: int, scale: float | None = None) -> np.ndarray:
+    """Proxy p[I, J] = s * qbar_I . kbar_J for every query block I and key block J.
+
+    The Abstract's pooled score; the kernel evaluates one row of it on chip and
+    never writes the map out.  Here the whole [Nb, Nb] map is formed on the CPU.
+    """
+    s = default_scale(q.shape[1], scale)
+    qb = block_means(q, block)
+    kb = block_means(k, block)
+    return s * (qb @ kb.T)
+
+
+def route(q: np.ndarray, k: np.ndarray, block: int, tau: float, scale: float | None = None):
+    """Query-dependent threshold routing (Sol-Attn Abstract).
+
+    keep[I, J] = p[I, J] >= max_J' p[I, J'] - tau   (inclusive).
+    Returns (keep bool [Nb, Nb], p [Nb, Nb], rowmax [Nb]).
+    """
+    tau = float(tau)
+    if math.isnan(tau) or tau < 0:
+        raise ValueError("tau must be >= 0 (or +inf)")
+    p = proxy_scores(q, k, block, scale)
+    m = p.max(axis=1)
+    keep = p >= (m - tau)[:, None]
+    return keep, p, m
+
+
+def attend_rows(q_rows: np.ndarray, k: np.ndarray, v: np.ndarray, keep_row: np.ndarray,
+                block: int, correction: bool, scale: float | None = None):
+    """Output and LSE of the rows of one query block, given its keep row.
+
+    q_rows: [n_I, D]; k: [N, D]; v: [N, Dv]; keep_row: bool [Nb].
+    Two passes over all logits of each row (exact logits of kept blocks, then
+    the correction logits of skipped blocks with multiplicity n_J), max, sums.
+    """
+    q_rows = np.asarray(q_rows, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    s = default_scale(q_rows.shape[1], scale)
+    N = k.shape[0]
+    ranges = block_ranges(N, block)
+    kept = [J for J in range(len(ranges)) if keep_row[J]]
+    skipped = [J for J in range(len(ranges)) if not keep_row[J]]
+
+    # exact logits s_ij over the tokens of the kept blocks
+    idx = np.concatenate([np.arange(*ranges[J]) for J in kept]) if kept else np.zeros(0, dtype=np.int64)
+    logits = s * (q_rows @ k[idx].T)                       # [n_I, n_kept_tokens]
+    weights_mult = np.ones(idx.shape[0])
+    values = v[idx]
+
+    if correction and skipped:
+        kbar = np.stack([k[slice(*ranges[J])].mean(axis=0) for J in skipped])
+        vbar = np.stack([v[slice(*ranges[J])].mean(axis=0) for J in skipped])
+        nJ = np.array([ranges[J][1] - ranges[J][0] for J in skipped], dtype=np.float64)
+        c = s * (q_rows @ kbar.T)                          # score columns of skipped blocks
+        logits = np.concatenate([logits, c], axis=1)
+        weights_mult = np.concatenate([weights_mult, nJ])
+        values = np.concatenate([values, vbar], axis=0)
+
+    M = logits.max(axis=1, keepdims=True)
+    w = weights_mult[None, :] * np.exp(logits - M)         # n_J copies -> weight n_J
+    Z = w.sum(axis=1, keepdims=True)
+    o = (w @ values) / Z
+    lse = M[:, 0] + np.log(Z[:, 0])
+    return o, lse
+
+
+def forward_head(q, k, v, block: int = 64, tau: float = math.inf, correction: bool = True,
+                 scale: float | None = None, keep: np.ndarray | None = None,
+                 qblocks=None):
+    """Sparse attention of one (batch, head): returns (o [N, Dv], lse [N], keep).
+
+    keep: optional externally supplied [Nb, Nb] mask replacing the routing
+    (used to evaluate the definition on a mask that differs from this oracle's
+    only inside the near-threshold band).  qblocks: optional iterable of query
+    block indices; rows of other blocks are left as NaN.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    N = q.shape[0]
+    if keep is None:
+        keep, _, _ = route(q, k, block, tau, scale)
+    ranges = block_ranges(N, block)
+    o = np.full((N, np.asarray(v).shape[1]), np.nan)
+    lse = np.full(N, np.nan)
+    for I in (range(len(ranges)) if qblocks is None else qblocks):
+        a, b = ranges[I]
+        o[a:b], lse[a:b] = attend_rows(q[a:b], k, v, keep[I], block, correction, scale)
+    return o, lse, keep
+
+
+def forward(q, k, v, block: int = 64, tau: float = math.inf, correction: bool = True,
+            scale: float | None = None):
+    """[B, H, N, D] batched form of forward_head; every (b, h) routes independently."""
+    q = np.asarray(q, dtype=np.float64)
+    B, H, N, _ = q.shape
+    o = np.empty(q.shape[:3] + (np.asarray(v).shape[3],))
+    lse = np.empty((B, H, N))
+    keep = np.empty((B, H, (N + block - 1) // block, (N + block - 1) // block), dtype=bool)
+    for b in range(B):
+        for h in range(H):
+            o[b, h], lse[b, h], keep[b, h] = forward_head(q[b, h], k[b, h], v[b, h], block, tau,
+                                                          correction, scale)
+    return o, lse, keep
+
+
+def dense_head(q, k, v, scale: float | None = None, rows=None):
+    """Dense bidirectional softmax attention of one head (the tau = inf limit).
+
+    The baseline every speedup on the Sol-Attn page is quoted against
+    (labelled "Dense").  rows: optional index array of query rows.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    s = default_scale(q.shape[1], scale)
+    qr = q if rows is None else q[rows]
+    logits = s * (qr @ k.T)
+    M = logits.max(axis=1, keepdims=True)
+    w = np.exp(logits - M)
+    Z = w.sum(axis=1, keepdims=True)
+    return (w @ v) / Z, M[:, 0] + np.log(Z[:, 0])
