@@ -1,0 +1,277 @@
+#!/usr/bin/env python3
+"""Benchmark of the on-the-fly block-sparse attention path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 720p] [--tau 2]
+
+A step is one sa_forward call (pool kernel + fused route/correct/attend
+kernel) over the whole workload, inputs resident in HBM.  Prints one JSON
+line on stdout; diagnostics go to stderr.
+
+value = computed-block TFLOP/s: sum over kept (query block, key block) pairs
+of 4*D*n_I*n_J, divided by the wall time of one call.  The roofline object
+covers the fused kernel, timed with HIP events recorded on the stream the
+library launches on, around each launch inside the timed region.  The
+cpu_baseline leg times the float64 CPU oracle on a bounded sample of the same
+workload (a few query blocks of one head) and reports it in the same unit.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+from block_sparse_attention_route_amd import api, synth  # noqa: E402
+
+METRIC = "sparse-attn ms/call + computed-block TFLOPS (% MFMA peak), 720p video DiT shape"
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_FP8_TFLOPS = 5000.0    # MI355X dense fp8 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fused_kernel_traffic.json")
+KERNEL_SOURCES = ["attn_mfma.hip", "sa_device.h", "sa_layout.h"]
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "block_sparse_attention_route_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def computed_block_flops(mask: np.ndarray, N: int, D: int) -> float:
+    """sum over kept (I, J) of 4*D*n_I*n_J for a [BH, Nb, Nb] 0/1 mask."""
+    Nb = mask.shape[-1]
+    n = np.full(Nb, 64.0)
+    n[-1] = N - 64 * (Nb - 1)
+    per_row = (mask.astype(np.float64) * n[None, None, :]).sum(axis=-1)   # [BH, Nb]
+    return float(4.0 * D * (per_row * n[None, :]).sum())
+
+
+def correction_flops(mask: np.ndarray, N: int, D: int) -> float:
+    """4*D*n_I per skipped (I, J) pair (score column and value of the correction)."""
+    Nb = mask.shape[-1]
+    n = np.full(Nb, 64.0)
+    n[-1] = N - 64 * (Nb - 1)
+    skipped = (1 - mask.astype(np.float64)).sum(axis=-1)
+    return float(4.0 * D * (skipped * n[None, :]).sum())
+
+
+def cpu_baseline(inp, wl, tau, o_gpu, budget_s: float):
+    """Time the float64 oracle on a bounded sample: query blocks of head (0, 0)."""
+    from oracle import attention as orc  # test infrastructure: cpu_baseline leg only
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        cores = 1
+    q, k, v = inp.head64(0, 0)
+    t0 = time.perf_counter()
+    keep, p, m = orc.route(q, k, wl.block, tau)
+    t_route = time.perf_counter() - t0
+    ranges = orc.block_ranges(wl.N, wl.block)
+    n = np.array([e - s for s, e in ranges], dtype=np.float64)
+    rng = np.random.default_rng(0)
+    order = [len(ranges) - 1] + list(rng.permutation(len(ranges) - 1))
+    flops, done, t_attend, maxerr = 0.0, [], 0.0, 0.0
+    o_g = o_gpu[0, 0].float().cpu().numpy()
+    for I in order:
+        t1 = time.perf_counter()
+        a, b = ranges[I]
+        o_ref, _ = orc.attend_rows(q[a:b], k, v, keep[I], wl.block, wl.correction)
+        t_attend += time.perf_counter() - t1
+        flops += 4.0 * wl.D * n[I] * float((keep[I] * n).sum())
+        maxerr = max(maxerr, float(np.abs(o_ref - o_g[a:b]).max()))
+        done.append(I)
+        if t_route + t_attend > budget_s:
+            break
+    elapsed = t_route + t_attend
+    nband = int((np.abs(p - (m - tau)[:, None]) < 1e-3).sum()) if math.isfinite(tau) else 0
+    return {
+        "value": flops / elapsed / 1e12,
+        "unit": "TFLOP/s",
+        "cores": int(cores),
+        "kind": "oracle",
+        "sample": (f"float64 numpy oracle, head (0,0) of {wl.name}: routing of all {len(ranges)} query blocks "
+                   f"({t_route:.2f} s) + attention of {len(done)} query blocks incl. the ragged last one "
+                   f"({t_attend:.2f} s); computed-block FLOP of the sample / time"),
+        "sample_max_abs_err_vs_gpu": maxerr,
+        "near_threshold_blocks_head0": nband,
+    }
+
+
+def main() -> None:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="720p", choices=sorted(synth.WORKLOADS))
+    ap.add_argument("--tau", type=float, default=None)
+    ap.add_argument("--no-correction", action="store_true")
+    ap.add_argument("--dense-steps", type=int, default=2)
+    ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: the path shards by (batch, head) with no exchange, "
+              "and runs with more than one GPU are not part of this build. Use --gpus 1.",
+              file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+
+    wl = synth.workload(args.workload)
+    tau = args.tau if args.tau is not None else wl.taus[0]
+    correction = wl.correction and not args.no_correction
+    grid = (wl.T, wl.Hg, wl.Wg)
+    t0 = time.time()
+    inp = synth.generate(wl)
+    log(f"generated {wl.name} B{wl.B} H{wl.H} N{wl.N} D{wl.D} {wl.dtype} in {time.time() - t0:.1f}s")
+    dev = torch.device("cuda:0")
+    q, k, v = inp.q.to(dev), inp.k.to(dev), inp.v.to(dev)
+    qs = inp.q_scale.to(dev) if inp.q_scale is not None else None
+    ks = inp.k_scale.to(dev) if inp.k_scale is not None else None
+    ws = torch.empty(api.sa_workspace_bytes(q, k, v, grid), dtype=torch.uint8, device=dev)
+    o = torch.empty(q.shape, dtype=v.dtype, device=dev)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
+    kept = torch.empty((wl.B, wl.H, wl.Nb), dtype=torch.int32, device=dev)
+
+    mask, kept_r = api.sa_route(q, k, v, grid, tau=tau, q_scale=qs, k_scale=ks)
+    torch.cuda.synchronize()
+    mask_np = mask.cpu().numpy().reshape(wl.B * wl.H, wl.Nb, wl.Nb)
+    del mask
+    f_exact = computed_block_flops(mask_np, wl.N, wl.D)
+    f_corr = correction_flops(mask_np, wl.N, wl.D) if correction else 0.0
+    f_dense = 4.0 * wl.B * wl.H * wl.N * wl.N * wl.D
+    density = float(mask_np.mean())
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record()
+        api.sa_pool(q, k, v, grid, tau=tau, correction=correction, workspace=ws, q_scale=qs, k_scale=ks)
+        if ev is not None:
+            ev[1].record()
+        api.sa_forward_pooled(q, k, v, grid, tau=tau, correction=correction, workspace=ws, q_scale=qs,
+                              k_scale=ks, out=o, lse=lse, kept=kept, want_kept=True)
+        if ev is not None:
+            ev[2].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for i in range(args.steps):
+        step(evs[i])
+    end.record()
+    torch.cuda.synchronize()
+    ms_step = start.elapsed_time(end) / args.steps
+    pool_ms = [e[0].elapsed_time(e[1]) for e in evs]
+    fused_ms = [e[1].elapsed_time(e[2]) for e in evs]
+    assert torch.equal(kept.cpu(), kept_r.cpu()), "fused routing disagrees with sa_route"
+
+    value = f_exact / (ms_step * 1e-3) / 1e12
+    fused_avg = float(np.mean(fused_ms))
+    achieved = f_exact / (fused_avg * 1e-3) / 1e12
+    peak = PEAK_BF16_TFLOPS
+    if wl.dtype == "fp8":
+        peak = 1.0 / (0.5 / PEAK_FP8_TFLOPS + 0.5 / PEAK_BF16_TFLOPS)   # QK^T fp8, PV bf16
+    pool_bytes = (wl.B * wl.H * wl.N * wl.D * (3 if wl.dtype == "f32" else 2) * 4 if wl.dtype == "f32"
+                  else wl.B * wl.H * wl.N * wl.D * ((1 if wl.dtype == "fp8" else 2) * 2 + 2))
+    pool_bytes += wl.B * wl.H * wl.Nb * wl.D * 4 * 3   # fp32 means written
+    if wl.dtype != "f32":
+        pool_bytes += wl.B * wl.H * wl.Nb * wl.D * 64 * 2   # regrouped V written
+    pool_avg = float(np.mean(pool_ms))
+
+    traffic = None
+    if os.path.exists(TRAFFIC_FILE):
+        with open(TRAFFIC_FILE) as f:
+            tr = json.load(f)
+        if tr.get("kernel_src_sha256") == kernel_source_hash() and tr.get("workload") == wl.name \
+                and float(tr.get("tau", -1)) == tau:
+            traffic = tr.get("bytes_per_launch")
+
+    # dense path at the same shape (the tau = inf baseline)
+    dense = None
+    if args.dense_steps > 0:
+        wsd = torch.empty(max(api.sa_dense_workspace_bytes(q, k, v, grid), 1), dtype=torch.uint8, device=dev)
+        od = torch.empty_like(o)
+        lsed = torch.empty_like(lse)
+        api.sa_dense_forward(q, k, v, grid, workspace=wsd, q_scale=qs, k_scale=ks, out=od, lse=lsed)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(args.dense_steps):
+            api.sa_dense_forward(q, k, v, grid, workspace=wsd, q_scale=qs, k_scale=ks, out=od, lse=lsed)
+        e1.record()
+        torch.cuda.synchronize()
+        dms = e0.elapsed_time(e1) / args.dense_steps
+        dense = {"ms": dms, "tflops": f_dense / (dms * 1e-3) / 1e12,
+                 "frac_peak": f_dense / (dms * 1e-3) / 1e12 / peak, "sparse_speedup": dms / ms_step}
+        del wsd, od, lsed
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(inp, wl, tau, o, args.cpu_budget)
+
+    out = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": {"bf16": "bf16", "f32": "f32", "fp8": "fp8e4m3-qk/bf16-pv"}[wl.dtype],
+        "data": "synthetic",
+        "config": {
+            "workload": (f"{wl.name} video-DiT self-attention: B{wl.B} H{wl.H} grid {wl.T}x{wl.Hg}x{wl.Wg} "
+                         f"N{wl.N} D{wl.D} {wl.dtype}, block 64, tau {tau:g}, correction "
+                         f"{'on' if correction else 'off'}"),
+            "B": wl.B, "H": wl.H, "N": wl.N, "D": wl.D, "tau": tau, "correction": correction,
+            "parallelism": "single GPU (heads independent)",
+        },
+        "frac_mfma_peak": value / peak,
+        "block_density": density,
+        "work_density": f_exact / f_dense,
+        "computed_block_tflop": f_exact / 1e12,
+        "correction_tflop": f_corr / 1e12,
+        "dense_equivalent_tflops": f_dense / (ms_step * 1e-3) / 1e12,
+        "pool": {"ms": pool_avg, "gbs": pool_bytes / (pool_avg * 1e-3) / 1e9,
+                 "frac_hbm": pool_bytes / (pool_avg * 1e-3) / 1e9 / PEAK_HBM_GBS, "bytes": pool_bytes},
+        "fused_kernel_ms": fused_avg,
+        "ms_per_call_min": float(np.min(np.add(pool_ms, fused_ms))),
+        "ms_per_call_p90": float(np.percentile(np.add(pool_ms, fused_ms), 90)),
+        "roofline": {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
+                     "frac": achieved / peak, "traffic": traffic,
+                     "kernel": "attn_kernel (fused route + correction + sparse flash attention)",
+                     "achieved_incl_correction": (f_exact + f_corr) / (fused_avg * 1e-3) / 1e12},
+        "dense": dense,
+        "cpu_baseline": cpu,
+        "kernel_src": kernel_source_hash(),
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,320 @@
+// C ABI of libsa_route (declared in include/sa_route.h): argument validation,
+// workspace carve-up and kernel launches.  Every check runs on the host
+// before anything is enqueued; a failed check returns a status and leaves a
+// message in a thread-local buffer.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "sa_kernels.h"
+#include "sa_layout.h"
+#include "sa_route.h"
+
+#define SA_API extern "C" __attribute__((visibility("default")))
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+sa_status fail(sa_status s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+sa_status ok() {
+  g_err[0] = '\0';
+  return SA_OK;
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+struct Req {
+  int64_t B, H, BH, N, Nb, Nbp;
+  int D;
+  int qk, v;
+  bool empty;
+  float scale, tau;
+  int correction;
+  sa::WsLayout ws;
+};
+
+sa_status check_shape_inputs(const sa_shape* sh, const sa_inputs* in, Req* r, bool dense,
+                             bool ptrs = true) {
+  if (!sh) return fail(SA_ERR_NULL, "shape is NULL");
+  if (!in) return fail(SA_ERR_NULL, "inputs is NULL");
+  if (sh->B < 0 || sh->H < 0 || sh->N < 0 || sh->T < 0 || sh->Hg < 0 || sh->Wg < 0)
+    return fail(SA_ERR_SHAPE, "negative dimension");
+  if (sh->D != 64 && sh->D != 128) return fail(SA_ERR_SHAPE, "D must be 64 or 128 (got %d)", sh->D);
+  const int64_t grid = (int64_t)sh->T * sh->Hg * sh->Wg;
+  if (grid != sh->N)
+    return fail(SA_ERR_SHAPE, "N (%d) != T*Hg*Wg (%lld)", sh->N, (long long)grid);
+  if (sh->N > SA_MAX_N) return fail(SA_ERR_SHAPE, "N (%d) exceeds SA_MAX_N (%d)", sh->N, SA_MAX_N);
+  const int qk = in->qk_dtype, v = in->v_dtype;
+  const bool pair_ok = (qk == SA_F32 && v == SA_F32) || (qk == SA_BF16 && v == SA_BF16) ||
+                       (qk == SA_FP8_E4M3 && v == SA_BF16);
+  if (!pair_ok) return fail(SA_ERR_DTYPE, "unsupported dtype pair (qk=%d, v=%d)", qk, v);
+  const bool fp8 = qk == SA_FP8_E4M3;
+  r->B = sh->B;
+  r->H = sh->H;
+  r->BH = (int64_t)sh->B * sh->H;
+  r->N = sh->N;
+  r->D = sh->D;
+  r->Nb = (r->N + SA_BLOCK - 1) / SA_BLOCK;
+  r->Nbp = (r->Nb + 63) / 64 * 64;
+  r->qk = qk;
+  r->v = v;
+  r->empty = r->BH * r->N == 0;
+  if (r->BH > (int64_t)1 << 24) return fail(SA_ERR_SHAPE, "B*H too large");
+  r->ws = sa::ws_layout(r->BH, r->N, r->D, v == SA_BF16, dense);
+  if (!ptrs) return SA_OK;  // sizing only: data pointers are not needed
+  if (!fp8 && (in->q_scale || in->k_scale))
+    return fail(SA_ERR_DTYPE, "q_scale/k_scale given for a non-fp8 qk_dtype");
+  if (r->empty) return SA_OK;
+  if (!in->q || !in->k || !in->v) return fail(SA_ERR_NULL, "q, k or v is NULL");
+  if (fp8 && (!in->q_scale || !in->k_scale))
+    return fail(SA_ERR_DTYPE, "fp8 qk_dtype needs q_scale and k_scale");
+  if (!aligned(in->q, 16) || !aligned(in->k, 16) || !aligned(in->v, 16))
+    return fail(SA_ERR_ALIGN, "q, k and v must be 16-byte aligned");
+  if (fp8 && (!aligned(in->q_scale, 4) || !aligned(in->k_scale, 4)))
+    return fail(SA_ERR_ALIGN, "scales must be 4-byte aligned");
+  return SA_OK;
+}
+
+sa_status check_params(const sa_params* p, Req* r) {
+  if (!p) return fail(SA_ERR_NULL, "params is NULL");
+  if (p->block != SA_BLOCK) return fail(SA_ERR_PARAM, "block must be %d (got %d)", SA_BLOCK, p->block);
+  if (std::isnan(p->tau) || p->tau < 0.f) return fail(SA_ERR_PARAM, "tau must be >= 0 or +inf");
+  if (p->correction != 0 && p->correction != 1) return fail(SA_ERR_PARAM, "correction must be 0 or 1");
+  if (!std::isfinite(p->scale)) return fail(SA_ERR_PARAM, "scale must be finite");
+  r->tau = p->tau;
+  r->correction = p->correction;
+  r->scale = p->scale > 0.f ? p->scale : 1.0f / std::sqrt((float)r->D);
+  return SA_OK;
+}
+
+sa_status check_ws(const void* ws, size_t ws_bytes, const Req& r) {
+  if (r.ws.total == 0) return SA_OK;
+  if (!ws) return fail(SA_ERR_NULL, "workspace is NULL");
+  if (!aligned(ws, 16)) return fail(SA_ERR_ALIGN, "workspace must be 16-byte aligned");
+  if (ws_bytes < r.ws.total)
+    return fail(SA_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", ws_bytes, r.ws.total);
+  return SA_OK;
+}
+
+sa_status check_out(const void* o, const float* lse, const int32_t* kept) {
+  if (!o || !lse) return fail(SA_ERR_NULL, "o or lse is NULL");
+  if (!aligned(o, 16)) return fail(SA_ERR_ALIGN, "o must be 16-byte aligned");
+  if (!aligned(lse, 4)) return fail(SA_ERR_ALIGN, "lse must be 4-byte aligned");
+  if (kept && !aligned(kept, 4)) return fail(SA_ERR_ALIGN, "kept must be 4-byte aligned");
+  return SA_OK;
+}
+
+template <typename T>
+T* at(void* ws, size_t off) {
+  return reinterpret_cast<T*>(static_cast<uint8_t*>(ws) + off);
+}
+
+sa::PoolArgs pool_args(const Req& r, const sa_inputs* in, void* ws, bool vt_only) {
+  sa::PoolArgs a{};
+  a.q = in->q;
+  a.k = in->k;
+  a.v = in->v;
+  a.q_scale = in->q_scale;
+  a.k_scale = in->k_scale;
+  a.BH = (int)r.BH;
+  a.N = (int)r.N;
+  a.Nb = (int)r.Nb;
+  a.Nbp = (int)r.Nbp;
+  a.D = r.D;
+  a.qk_elt = r.qk;
+  a.v_elt = r.v;
+  a.vt_only = vt_only;
+  if (!vt_only) {
+    a.qbar = at<float>(ws, r.ws.qbar);
+    a.kbar = at<float>(ws, r.ws.kbar);
+    a.vbar = at<float>(ws, r.ws.vbar);
+    if (r.v == SA_BF16) {
+      a.kbar16 = at<uint16_t>(ws, r.ws.kbar16);
+      a.vbarT16 = at<uint16_t>(ws, r.ws.vbarT16);
+    }
+  }
+  if (r.v == SA_BF16) a.vt16 = at<uint16_t>(ws, r.ws.vt16);
+  return a;
+}
+
+sa::AttnArgs attn_args(const Req& r, const sa_inputs* in, void* o, float* lse, int32_t* kept,
+                       void* ws, bool sparse) {
+  sa::AttnArgs a{};
+  a.q = in->q;
+  a.k = in->k;
+  a.v = in->v;
+  a.q_scale = in->q_scale;
+  a.k_scale = in->k_scale;
+  if (sparse) {
+    a.qbar = at<float>(ws, r.ws.qbar);
+    a.kbar = at<float>(ws, r.ws.kbar);
+    a.vbar = at<float>(ws, r.ws.vbar);
+    if (r.v == SA_BF16) {
+      a.kbar16 = at<uint16_t>(ws, r.ws.kbar16);
+      a.vbarT16 = at<uint16_t>(ws, r.ws.vbarT16);
+    }
+  }
+  if (r.v == SA_BF16) a.vt16 = at<uint16_t>(ws, r.ws.vt16);
+  a.o = o;
+  a.lse = lse;
+  a.kept = kept;
+  a.BH = (int)r.BH;
+  a.N = (int)r.N;
+  a.Nb = (int)r.Nb;
+  a.Nbp = (int)r.Nbp;
+  a.D = r.D;
+  a.qk_elt = r.qk;
+  a.v_elt = r.v;
+  a.scale = r.scale;
+  a.tau = r.tau;
+  a.correction = r.correction;
+  a.sparse = sparse;
+  return a;
+}
+
+sa_status hip_status(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(SA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+sa_status run_attn(const Req& r, const sa_inputs* in, void* o, float* lse, int32_t* kept, void* ws,
+                   bool sparse, hipStream_t st) {
+  const sa::AttnArgs a = attn_args(r, in, o, lse, kept, ws, sparse);
+  const hipError_t e = (r.qk == SA_F32) ? sa::launch_attn_f32(a, st) : sa::launch_attn_mfma(a, st);
+  return hip_status(e, "attention kernel launch");
+}
+
+}  // namespace
+
+SA_API int32_t sa_abi_version(void) { return SA_ABI_VERSION; }
+
+SA_API const char* sa_status_string(sa_status s) {
+  switch (s) {
+    case SA_OK: return "SA_OK";
+    case SA_ERR_NULL: return "SA_ERR_NULL: a required pointer is NULL";
+    case SA_ERR_SHAPE: return "SA_ERR_SHAPE: invalid shape";
+    case SA_ERR_PARAM: return "SA_ERR_PARAM: invalid routing parameter";
+    case SA_ERR_DTYPE: return "SA_ERR_DTYPE: unsupported dtype combination";
+    case SA_ERR_ALIGN: return "SA_ERR_ALIGN: misaligned pointer";
+    case SA_ERR_WORKSPACE: return "SA_ERR_WORKSPACE: workspace too small";
+    case SA_ERR_UNSUPPORTED: return "SA_ERR_UNSUPPORTED: not implemented";
+    case SA_ERR_HIP: return "SA_ERR_HIP: HIP runtime error";
+  }
+  return "unknown sa_status";
+}
+
+SA_API const char* sa_last_error(void) { return g_err; }
+
+SA_API size_t sa_workspace_bytes(const sa_shape* shape, const sa_params* params, const sa_inputs* in) {
+  Req r{};
+  if (check_shape_inputs(shape, in, &r, false, false) != SA_OK) return 0;
+  if (params) {
+    if (check_params(params, &r) != SA_OK) return 0;
+  }
+  return r.ws.total;
+}
+
+SA_API size_t sa_dense_workspace_bytes(const sa_shape* shape, const sa_inputs* in) {
+  Req r{};
+  if (check_shape_inputs(shape, in, &r, true, false) != SA_OK) return 0;
+  return r.ws.total;
+}
+
+SA_API sa_status sa_pool(const sa_shape* shape, const sa_params* params, const sa_inputs* in,
+                         void* ws, size_t ws_bytes, void* stream) {
+  Req r{};
+  sa_status s;
+  if ((s = check_shape_inputs(shape, in, &r, false)) != SA_OK) return s;
+  if ((s = check_params(params, &r)) != SA_OK) return s;
+  if (r.empty) return ok();
+  if ((s = check_ws(ws, ws_bytes, r)) != SA_OK) return s;
+  return hip_status(sa::launch_pool(pool_args(r, in, ws, false), (hipStream_t)stream),
+                    "pool kernel launch");
+}
+
+SA_API sa_status sa_route(const sa_shape* shape, const sa_params* params, const sa_inputs* in,
+                          uint8_t* mask, int32_t* kept, void* ws, size_t ws_bytes, void* stream) {
+  Req r{};
+  sa_status s;
+  if ((s = check_shape_inputs(shape, in, &r, false)) != SA_OK) return s;
+  if ((s = check_params(params, &r)) != SA_OK) return s;
+  if (r.empty) return ok();
+  if (!mask) return fail(SA_ERR_NULL, "mask is NULL");
+  if (kept && !aligned(kept, 4)) return fail(SA_ERR_ALIGN, "kept must be 4-byte aligned");
+  if ((s = check_ws(ws, ws_bytes, r)) != SA_OK) return s;
+  hipStream_t st = (hipStream_t)stream;
+  if ((s = hip_status(sa::launch_pool(pool_args(r, in, ws, false), st), "pool kernel launch")) != SA_OK)
+    return s;
+  sa::RouteArgs a{};
+  a.qbar = at<float>(ws, r.ws.qbar);
+  a.kbar = at<float>(ws, r.ws.kbar);
+  a.BH = (int)r.BH;
+  a.Nb = (int)r.Nb;
+  a.D = r.D;
+  a.scale = r.scale;
+  a.tau = r.tau;
+  a.mask = mask;
+  a.kept = kept;
+  return hip_status(sa::launch_route(a, st), "route kernel launch");
+}
+
+SA_API sa_status sa_forward_pooled(const sa_shape* shape, const sa_params* params, const sa_inputs* in,
+                                   void* o, float* lse, int32_t* kept, void* ws, size_t ws_bytes,
+                                   void* stream) {
+  Req r{};
+  sa_status s;
+  if ((s = check_shape_inputs(shape, in, &r, false)) != SA_OK) return s;
+  if ((s = check_params(params, &r)) != SA_OK) return s;
+  if (r.empty) return ok();
+  if ((s = check_out(o, lse, kept)) != SA_OK) return s;
+  if ((s = check_ws(ws, ws_bytes, r)) != SA_OK) return s;
+  return run_attn(r, in, o, lse, kept, ws, true, (hipStream_t)stream);
+}
+
+SA_API sa_status sa_forward(const sa_shape* shape, const sa_params* params, const sa_inputs* in,
+                            void* o, float* lse, int32_t* kept, void* ws, size_t ws_bytes,
+                            void* stream) {
+  Req r{};
+  sa_status s;
+  if ((s = check_shape_inputs(shape, in, &r, false)) != SA_OK) return s;
+  if ((s = check_params(params, &r)) != SA_OK) return s;
+  if (r.empty) return ok();
+  if ((s = check_out(o, lse, kept)) != SA_OK) return s;
+  if ((s = check_ws(ws, ws_bytes, r)) != SA_OK) return s;
+  hipStream_t st = (hipStream_t)stream;
+  if ((s = hip_status(sa::launch_pool(pool_args(r, in, ws, false), st), "pool kernel launch")) != SA_OK)
+    return s;
+  return run_attn(r, in, o, lse, kept, ws, true, st);
+}
+
+SA_API sa_status sa_dense_forward(const sa_shape* shape, float scale, const sa_inputs* in, void* o,
+                                  float* lse, void* ws, size_t ws_bytes, void* stream) {
+  Req r{};
+  sa_status s;
+  if ((s = check_shape_inputs(shape, in, &r, true)) != SA_OK) return s;
+  if (!std::isfinite(scale)) return fail(SA_ERR_PARAM, "scale must be finite");
+  r.scale = scale > 0.f ? scale : 1.0f / std::sqrt((float)r.D);
+  r.tau = INFINITY;
+  r.correction = 0;
+  if (r.empty) return ok();
+  if ((s = check_out(o, lse, nullptr)) != SA_OK) return s;
+  if ((s = check_ws(ws, ws_bytes, r)) != SA_OK) return s;
+  hipStream_t st = (hipStream_t)stream;
+  if (r.v == SA_BF16) {
+    if ((s = hip_status(sa::launch_pool(pool_args(r, in, ws, true), st), "regroup kernel launch")) !=
+        SA_OK)
+      return s;
+  }
+  return run_attn(r, in, o, lse, nullptr, ws, false, st);
+}

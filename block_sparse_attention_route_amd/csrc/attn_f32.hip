@@ -1,0 +1,163 @@
+// Float32 variant of the fused block-sparse attention (and of dense
+// attention), for float32 Q/K/V.  Same method as the MFMA kernel -- on-chip
+// routing of each query block by the shared float32 routine, the skipped
+// blocks folded in as n_J copies of their mean key and value, exact attention
+// over the kept blocks, one online softmax (Sol-Attn project page, section
+// "Abstract") -- computed with float32 FMAs on the vector ALUs: gfx950's
+// matrix cores have no full-rate float32 path, and this variant exists for
+// full-precision results rather than speed.
+//
+// One wave per query block; lane i owns query row 64*I + i, holds q_i and its
+// output accumulator in registers, and reads keys and values broadcast from
+// LDS, 16 at a time, with natural exp and one rescale per group.
+#include "sa_device.h"
+#include "sa_kernels.h"
+
+namespace sa {
+namespace {
+
+constexpr int kGroup = 16;
+
+template <int D, bool SPARSE>
+__global__ __launch_bounds__(64) void attn_f32_kernel(AttnArgs a) {
+  const int N = a.N, Nb = a.Nb;
+  const int bh = blockIdx.y;
+  const int I = blockIdx.x;
+  const int lane = threadIdx.x;
+
+  __shared__ __attribute__((aligned(16))) float kt[kBlock * D];
+  __shared__ __attribute__((aligned(16))) float vt[kBlock * D];
+  __shared__ float lw[kBlock];          // log-multiplicity of each staged key
+  __shared__ float p[kMaxNb];
+  __shared__ uint8_t flags[SPARSE ? kMaxNb : 1];
+  __shared__ float qb[2 * D];
+  __shared__ float redf[8];
+  __shared__ int redi[8];
+  __shared__ int counts[2];
+
+  if constexpr (SPARSE) {
+    for (int d = lane; d < D; d += 64) {
+      qb[d] = a.qbar[((size_t)bh * Nb + I) * D + d];
+      qb[D + d] = 0.f;
+    }
+    __syncthreads();
+    proxy_row_pair<D, 64>(qb, a.kbar + (size_t)bh * Nb * D, Nb, a.scale, false, p);
+    __syncthreads();
+    threshold_rows<64>(p, Nb, false, a.tau, flags, redf, redi, counts);
+    if (a.kept && lane == 0) a.kept[(size_t)bh * Nb + I] = counts[0];
+  }
+
+  const int row = I * kBlock + lane;
+  const bool rv = row < N;
+  const float* qsrc = reinterpret_cast<const float*>(a.q) + ((size_t)bh * N + row) * D;
+  float q[D], acc[D];
+#pragma unroll
+  for (int d = 0; d < D; ++d) {
+    q[d] = rv ? qsrc[d] : 0.f;
+    acc[d] = 0.f;
+  }
+  float m = kNegInf, l = 0.f;
+
+  // online-softmax update with `cnt` staged keys (kt, vt, lw)
+  auto consume = [&](int cnt) {
+    for (int g0 = 0; g0 < cnt; g0 += kGroup) {
+      float x[kGroup];
+      float mg = kNegInf;
+#pragma unroll
+      for (int t = 0; t < kGroup; ++t) {
+        float s = 0.f;
+        if (g0 + t < cnt) {
+          const float* kr = kt + (g0 + t) * D;
+#pragma unroll
+          for (int d = 0; d < D; ++d) s = fmaf(q[d], kr[d], s);
+          x[t] = s * a.scale + lw[g0 + t];
+        } else {
+          x[t] = kNegInf;
+        }
+        mg = fmaxf(mg, x[t]);
+      }
+      const float mnew = fmaxf(m, mg);
+      const float alpha = (m == kNegInf) ? 0.f : expf(m - mnew);
+      l *= alpha;
+#pragma unroll
+      for (int d = 0; d < D; ++d) acc[d] *= alpha;
+#pragma unroll
+      for (int t = 0; t < kGroup; ++t) {
+        if (g0 + t < cnt) {
+          const float w = expf(x[t] - mnew);
+          l += w;
+          const float* vr = vt + (g0 + t) * D;
+#pragma unroll
+          for (int d = 0; d < D; ++d) acc[d] = fmaf(w, vr[d], acc[d]);
+        }
+      }
+      m = mnew;
+    }
+  };
+
+  const float* kin = reinterpret_cast<const float*>(a.k) + (size_t)bh * N * D;
+  const float* vin = reinterpret_cast<const float*>(a.v) + (size_t)bh * N * D;
+
+  // correction: skipped blocks as n_J copies of (kbar_J, vbar_J), 64 at a time
+  if (SPARSE && a.correction) {
+    const int ntail = N - (Nb - 1) * kBlock;
+    for (int J0 = 0; J0 < Nb; J0 += kBlock) {
+      int cnt = 0;
+      for (int J = J0; J < min(Nb, J0 + kBlock); ++J) {
+        if (flags[J] & 1) continue;
+        const float* kb = a.kbar + ((size_t)bh * Nb + J) * D;
+        const float* vb = a.vbar + ((size_t)bh * Nb + J) * D;
+        for (int d = lane; d < D; d += 64) {
+          kt[cnt * D + d] = kb[d];
+          vt[cnt * D + d] = vb[d];
+        }
+        if (lane == 0) lw[cnt] = logf((float)(J == Nb - 1 ? ntail : kBlock));
+        ++cnt;
+      }
+      __syncthreads();
+      consume(cnt);
+      __syncthreads();
+    }
+  }
+
+  // exact attention over the kept blocks (all blocks when dense)
+  for (int J = 0; J < Nb; ++J) {
+    if (SPARSE && !(flags[J] & 1)) continue;
+    const int n = min(kBlock, N - J * kBlock);
+    for (int x = lane; x < n * D; x += 64) {
+      kt[x] = kin[(size_t)J * kBlock * D + x];
+      vt[x] = vin[(size_t)J * kBlock * D + x];
+    }
+    if (lane < n) lw[lane] = 0.f;
+    __syncthreads();
+    consume(n);
+    __syncthreads();
+  }
+
+  if (rv) {
+    const float inv = 1.f / l;
+    float* orow = reinterpret_cast<float*>(a.o) + ((size_t)bh * N + row) * D;
+#pragma unroll
+    for (int d = 0; d < D; ++d) orow[d] = acc[d] * inv;
+    a.lse[(size_t)bh * N + row] = m + logf(l);
+  }
+}
+
+template <int D>
+hipError_t launch_d(const AttnArgs& a, hipStream_t st) {
+  const dim3 grid(a.Nb, a.BH);
+  if (a.sparse)
+    hipLaunchKernelGGL((attn_f32_kernel<D, true>), grid, dim3(64), 0, st, a);
+  else
+    hipLaunchKernelGGL((attn_f32_kernel<D, false>), grid, dim3(64), 0, st, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_attn_f32(const AttnArgs& a, hipStream_t st) {
+  if (a.BH == 0 || a.N == 0) return hipSuccess;
+  return a.D == 64 ? launch_d<64>(a, st) : launch_d<128>(a, st);
+}
+
+}  // namespace sa

@@ -1,0 +1,423 @@
+// Fused on-the-fly block-sparse flash attention for gfx950 (bf16 MFMA; fp8
+// QK^T variant), and the dense attention it reduces to.
+//
+// Sol-Attn project page (section "Abstract"): routing by a query-dependent
+// threshold, sparse computation and an approximate correction of the skipped
+// blocks run in a single online-softmax pass, with blocks selected on chip and
+// no proxy map materialised.  Sol-Engine README (section "Sol-Attention"):
+// only the most relevant key blocks are computed, plus a light-weight
+// compensating operation.  Per workgroup (two adjacent 64-token query blocks
+// of one head) this kernel:
+//
+//   1. route: evaluates the proxy rows p_IJ = s * qbar_I . kbar_J of both
+//      query blocks into LDS (the shared float32 routine of sa_device.h),
+//      thresholds them at rowmax - tau and compacts the union of the kept
+//      key blocks into an index list in LDS -- nothing is written to HBM;
+//   2. correct: streams the block means as "virtual keys": virtual key J has
+//      key kbar_J, value vbar_J and log-multiplicity log(n_J), and is masked
+//      for a query block that keeps J.  Its logit s * q_i . kbar_J is entry
+//      (i, J) of s * Q_I Kbar^T -- the below-threshold score column of block
+//      J -- and it enters the same running max / sum as the exact keys;
+//   3. exact: flash attention over the kept key blocks (the union list; the
+//      waves of a query block that does not keep a block skip it), with the
+//      ragged last key block masked;
+//   4. epilogue: O = acc / l in bf16 and the natural-log LSE.
+//
+// Tiling.  256 threads = 4 waves; wave w owns 32 query rows (query block
+// 2*pair + w/2, rows 32*(w%2) ..) against the full 64-key tile.  Products use
+// v_mfma_f32_32x32x16_bf16 with the roles transposed, S^T = K Q^T and
+// O^T = V^T P^T: a lane owns one query column, so the softmax row max and sum
+// are lane-local plus one exchange with lane^32, and the exponentiated scores
+// are already the B operand of the PV product.  The MFMA row order of K is
+// permuted (bits 2 and 3 swapped) so that the keys a lane holds after S^T are
+// exactly the keys its PV operand needs.  K tiles are row-major and V tiles
+// arrive pre-transposed (d-major) from the pool step; both are loaded straight
+// from global memory into double-buffered LDS (global_load_lds_dwordx4), with
+// an XOR swizzle on 16-byte chunks that keeps the MFMA operand reads
+// conflict-free.  Workgroup ids are remapped so each XCD walks a contiguous
+// range of query blocks (shared key blocks stay in that XCD's L2).
+#include "sa_device.h"
+#include "sa_kernels.h"
+
+namespace sa {
+namespace {
+
+constexpr int kThreads = 256;
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(1))) void gbl_void_t;
+
+// Key row that MFMA row m of a 32-key tile reads: swap bits 2 and 3.
+__device__ __forceinline__ int kperm(int m) { return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1); }
+
+// Key (within a 32-key tile) of accumulator element r of S^T, lane half h.
+__device__ __forceinline__ int key_of(int r, int h) { return r < 8 ? 8 * h + r : 8 + 8 * h + r; }
+
+template <int CPR>
+__device__ __forceinline__ int swz_any(int row, int chunk) {
+  if constexpr (CPR == 4) {
+    return chunk ^ ((row >> 2) & 3);
+  } else {
+    return swz<CPR>(row, chunk);
+  }
+}
+
+// 16 bytes from global straight into LDS.  The LDS destination of lane l is
+// lds_wave_base + 16*l; lds_wave_base must be the same for the whole wave.
+__device__ __forceinline__ void g2lds16(const void* gsrc, void* lds_wave_base) {
+  __builtin_amdgcn_global_load_lds((gbl_void_t*)gsrc, (lds_void_t*)lds_wave_base, 16, 0, 0);
+}
+
+template <int NT>
+__device__ __forceinline__ void build_union(const uint8_t* __restrict__ flags, int Nb,
+                                            uint16_t* __restrict__ ulist, int* total, int* wsum) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int seg = (Nb + NT - 1) / NT;
+  const int j0 = min(Nb, tid * seg), j1 = min(Nb, j0 + seg);
+  int cnt = 0;
+  for (int j = j0; j < j1; ++j) cnt += flags[j] != 0;
+  int x = cnt;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(x, off);
+    if (lane >= off) x += y;
+  }
+  if (lane == 63) wsum[wave] = x;
+  __syncthreads();
+  int base = 0;
+  for (int w = 0; w < wave; ++w) base += wsum[w];
+  int pos = base + x - cnt;
+  for (int j = j0; j < j1; ++j) {
+    const int f = flags[j];
+    if (f) ulist[pos++] = (uint16_t)(j | (f << 12));
+  }
+  if (tid == NT - 1) *total = base + x;
+  __syncthreads();
+}
+
+template <int D>
+struct Cfg {
+  static constexpr int KS = D / 16;          // k-steps of S^T (bf16 K)
+  static constexpr int DT = D / 32;          // 32-row d tiles of O^T
+  static constexpr int KROW16 = 2 * D;       // bytes of a bf16 K row
+  static constexpr int CPR16 = KROW16 / 16;  // 16-byte chunks per bf16 K row
+  static constexpr int KROW8 = D;            // bytes of an fp8 K row
+  static constexpr int CPR8 = KROW8 / 16;
+  static constexpr int KTILE = 64 * KROW16;  // K buffer bytes (sized for bf16)
+  static constexpr int VTILE = D * 128;      // V^T tile: D rows of 64 bf16 keys
+  static constexpr int STAGE = 2 * (KTILE + VTILE);
+  static constexpr int PROXY = 2 * kMaxNb * 4;
+  static constexpr int SMEM = STAGE > PROXY ? STAGE : PROXY;
+};
+
+template <int D, bool SPARSE, bool FP8>
+__global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnArgs a) {
+  using C = Cfg<D>;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[C::SMEM];
+  __shared__ uint8_t flags[SPARSE ? kMaxNb : 1];
+  __shared__ uint16_t ulist[SPARSE ? kMaxNb : 1];
+  __shared__ float qb[SPARSE ? 2 * D : 1];
+  __shared__ float redf[8];
+  __shared__ int redi[8];
+  __shared__ int counts[2];
+  __shared__ int nunion_s;
+
+  const int N = a.N, Nb = a.Nb;
+  const int npairs = (Nb + 1) >> 1;
+  const int G = a.BH * npairs;
+  const int tile = xcd_remap((int)blockIdx.x, G);
+  const int bh = tile / npairs;
+  const int pair = tile - bh * npairs;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int qsel = wave >> 1, qhalf = wave & 1;
+  const int h = lane >> 5, l32 = lane & 31;
+  const int I = 2 * pair + qsel;
+  const bool qvalid = I < Nb;
+  const bool two = 2 * pair + 1 < Nb;
+  const int ntail = N - (Nb - 1) * kBlock;  // tokens in the last block
+
+  // ---------------------------------------------------------------- 1. route
+  int nvirt = 0, nunion = Nb;
+  if constexpr (SPARSE) {
+    if (tid < 2 * D) {
+      const int r = tid / D, d = tid % D;
+      const int Ir = 2 * pair + r;
+      qb[tid] = (Ir < Nb) ? a.qbar[((size_t)bh * Nb + Ir) * D + d] : 0.f;
+    }
+    __syncthreads();
+    float* p = reinterpret_cast<float*>(smem);
+    proxy_row_pair<D, kThreads>(qb, a.kbar + (size_t)bh * Nb * D, Nb, a.scale, two, p);
+    __syncthreads();
+    threshold_rows<kThreads>(p, Nb, two, a.tau, flags, redf, redi, counts);
+    build_union<kThreads>(flags, Nb, ulist, &nunion_s, redi);
+    nunion = nunion_s;
+    if (a.kept && tid == 0) {
+      a.kept[(size_t)bh * Nb + 2 * pair] = counts[0];
+      if (two) a.kept[(size_t)bh * Nb + 2 * pair + 1] = counts[1];
+    }
+    if (a.correction) nvirt = a.Nbp / 64;
+  }
+  const int ntiles = nvirt + nunion;
+
+  // --------------------------------------- query operands (B of S^T = K Q^T)
+  const int qrow = I * kBlock + 32 * qhalf + l32;  // this lane's query row
+  const bool rowvalid = qvalid && qrow < N;
+  const size_t qtok = (size_t)bh * N + qrow;
+  bf16x8 qr[C::KS];
+  uint64_t q8[FP8 ? C::KS : 1];
+#pragma unroll
+  for (int ks = 0; ks < C::KS; ++ks) {
+    const int d0 = 16 * ks + 8 * h;
+    if constexpr (FP8) {
+      uint64_t w = 0;
+      if (rowvalid) w = *reinterpret_cast<const uint64_t*>(reinterpret_cast<const uint8_t*>(a.q) + qtok * D + d0);
+      q8[ks] = w;
+      bf16x8 x;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[e] = static_cast<__bf16>(fp8e4m3_to_f32((uint32_t)(w >> (8 * e)) & 0xFFu));
+      qr[ks] = x;
+    } else {
+      bf16x8 x = {};
+      if (rowvalid) x = *reinterpret_cast<const bf16x8*>(reinterpret_cast<const uint16_t*>(a.q) + qtok * D + d0);
+      qr[ks] = x;
+    }
+  }
+  float qscale = 1.f;
+  if constexpr (FP8) qscale = qvalid ? a.q_scale[(size_t)bh * Nb + I] : 0.f;
+
+  // ------------------------------------------------------------ LDS staging
+  auto Kbuf = [&](int buf) -> uint8_t* { return smem + buf * C::KTILE; };
+  auto Vbuf = [&](int buf) -> uint8_t* { return smem + 2 * C::KTILE + buf * C::VTILE; };
+  auto tile_block = [&](int it) -> int {
+    if constexpr (SPARSE) return ulist[it - nvirt] & 0xFFF;
+    return it;
+  };
+
+  // Issue the global->LDS copies of tile `it` into buffer `buf`.  Wave w's
+  // i-th copy fills LDS bytes [(w + 4i) KiB, +1 KiB); lane l writes 16 bytes
+  // at +16*l, i.e. physical chunk pc of row r, which holds logical chunk
+  // pc ^ swz(r).  Rows past the end of the sequence re-read the last valid
+  // row (finite data; those keys are masked).
+  auto issue_tile = [&](int it, int buf) {
+    const uint8_t* ksrc;
+    const uint8_t* vsrc;
+    int kvalid = 64;
+    bool k8 = false;
+    if (it < nvirt) {
+      ksrc = reinterpret_cast<const uint8_t*>(a.kbar16 + ((size_t)bh * a.Nbp + 64 * it) * D);
+      vsrc = reinterpret_cast<const uint8_t*>(a.vbarT16 + ((size_t)bh * (a.Nbp / 64) + it) * D * 64);
+    } else {
+      const int J = tile_block(it);
+      k8 = FP8;
+      ksrc = reinterpret_cast<const uint8_t*>(a.k) + ((size_t)bh * N + (size_t)J * kBlock) * D * (FP8 ? 1 : 2);
+      vsrc = reinterpret_cast<const uint8_t*>(a.vt16 + ((size_t)bh * Nb + J) * D * kBlock);
+      kvalid = min(kBlock, N - J * kBlock);
+    }
+    uint8_t* kb = Kbuf(buf);
+    if (k8) {
+#pragma unroll
+      for (int i = 0; i < C::KTILE / 2 / 4096; ++i) {
+        const int P = (wave + 4 * i) * 1024 + 16 * lane;
+        const int row = P / C::KROW8, pc = (P % C::KROW8) / 16;
+        const int src_row = min(row, kvalid - 1);
+        g2lds16(ksrc + src_row * C::KROW8 + swz_any<C::CPR8>(row, pc) * 16, kb + (wave + 4 * i) * 1024);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < C::KTILE / 4096; ++i) {
+        const int P = (wave + 4 * i) * 1024 + 16 * lane;
+        const int row = P / C::KROW16, pc = (P % C::KROW16) / 16;
+        const int src_row = min(row, kvalid - 1);
+        g2lds16(ksrc + src_row * C::KROW16 + swz<C::CPR16>(row, pc) * 16, kb + (wave + 4 * i) * 1024);
+      }
+    }
+    uint8_t* vb = Vbuf(buf);
+#pragma unroll
+    for (int i = 0; i < C::VTILE / 4096; ++i) {
+      const int P = (wave + 4 * i) * 1024 + 16 * lane;
+      const int row = P / 128, pc = (P % 128) / 16;
+      g2lds16(vsrc + row * 128 + swz<8>(row, pc) * 16, vb + (wave + 4 * i) * 1024);
+    }
+  };
+
+  // ----------------------------------------------------- online-softmax state
+  f32x16 acc[C::DT];
+#pragma unroll
+  for (int dt = 0; dt < C::DT; ++dt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[dt][r] = 0.f;
+  float m_run = kNegInf, l_run = 0.f;
+
+  const float c2_base = a.scale * kLog2e;  // logits in log2 units
+  const float log2_tail = log2f((float)ntail);
+
+  // -------------------------------------------------------------- main loop
+  if (ntiles > 0) issue_tile(0, 0);
+  for (int it = 0; it < ntiles; ++it) {
+    const int buf = it & 1;
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (it + 1 < ntiles) issue_tile(it + 1, buf ^ 1);
+
+    const bool virt = it < nvirt;
+    int J = 0;
+    bool active = qvalid;
+    if (!virt) {
+      J = tile_block(it);
+      if constexpr (SPARSE) active = active && ((ulist[it - nvirt] >> (12 + qsel)) & 1);
+    }
+    if (!active) continue;
+
+    // ---- S^T = K Q^T for the 64 keys of the tile (two 32-key MFMA tiles)
+    const uint8_t* Kb = Kbuf(buf);
+    f32x16 s[2];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[kt][r] = 0.f;
+    float c2 = c2_base * qscale;
+    bool k8 = false;
+    if constexpr (FP8) {
+      if (!virt) {
+        k8 = true;
+        c2 *= a.k_scale[(size_t)bh * Nb + J];
+      }
+    }
+    if (k8) {
+      if constexpr (FP8) {
+#pragma unroll
+        for (int ks = 0; ks < C::KS; ++ks) {
+#pragma unroll
+          for (int kt = 0; kt < 2; ++kt) {
+            const int krow = 32 * kt + kperm(l32);
+            const uint64_t ka = *reinterpret_cast<const uint64_t*>(
+                Kb + krow * C::KROW8 + swz_any<C::CPR8>(krow, ks) * 16 + 8 * h);
+            s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_fp8_fp8((long)ka, (long)q8[ks], s[kt], 0, 0, 0);
+          }
+        }
+      }
+    } else {
+#pragma unroll
+      for (int ks = 0; ks < C::KS; ++ks) {
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt) {
+          const int krow = 32 * kt + kperm(l32);
+          const bf16x8 ka = *reinterpret_cast<const bf16x8*>(
+              Kb + krow * C::KROW16 + swz<C::CPR16>(krow, 2 * ks + h) * 16);
+          s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qr[ks], s[kt], 0, 0, 0);
+        }
+      }
+    }
+
+    // ---- scaled logits (log2 units) with the tile's mask / log-multiplicity
+    float x[2][16];
+    const bool tail = !virt && J == Nb - 1 && ntail < kBlock;
+    if (virt) {
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int Jv = 64 * it + 32 * kt + key_of(r, h);
+          const bool live = Jv < Nb && !((flags[Jv < Nb ? Jv : 0] >> qsel) & 1);
+          const float w = (Jv == Nb - 1) ? log2_tail : 6.0f;  // log2(n_J): 64 except the tail
+          x[kt][r] = live ? fmaf(s[kt][r], c2, w) : kNegInf;
+        }
+    } else if (tail) {
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          x[kt][r] = (32 * kt + key_of(r, h) < ntail) ? s[kt][r] * c2 : kNegInf;
+    } else {
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) x[kt][r] = s[kt][r] * c2;
+    }
+
+    // ---- online softmax (row = this lane's query; keys split with lane^32)
+    float mt = kNegInf;
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mt = fmaxf(mt, x[kt][r]);
+    mt = fmaxf(mt, __shfl_xor(mt, 32));
+    const float mnew = fmaxf(m_run, mt);
+    const float muse = (mnew == kNegInf) ? 0.f : mnew;
+    if (__any(mnew > m_run)) {
+      const float alpha = __builtin_amdgcn_exp2f(m_run - muse);
+      l_run *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < C::DT; ++dt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[dt][r] *= alpha;
+    }
+    m_run = mnew;
+    bf16x8 pb[4];
+    float rs = 0.f;
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float pr = __builtin_amdgcn_exp2f(x[kt][r] - muse);
+        rs += pr;
+        pb[2 * kt + (r >> 3)][r & 7] = static_cast<__bf16>(pr);
+      }
+    l_run += rs;
+
+    // ---- O^T += V^T P^T
+    const uint8_t* Vb = Vbuf(buf);
+#pragma unroll
+    for (int dt = 0; dt < C::DT; ++dt) {
+      const int vrow = 32 * dt + l32;
+#pragma unroll
+      for (int k4 = 0; k4 < 4; ++k4) {
+        const bf16x8 va = *reinterpret_cast<const bf16x8*>(Vb + vrow * 128 + swz<8>(vrow, 2 * k4 + h) * 16);
+        acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[k4], acc[dt], 0, 0, 0);
+      }
+    }
+  }
+
+  // --------------------------------------------------------------- 4. epilogue
+  const float lt = l_run + __shfl_xor(l_run, 32);
+  if (rowvalid) {
+    const float inv = 1.f / lt;
+    uint16_t* orow = reinterpret_cast<uint16_t*>(a.o) + qtok * D;
+#pragma unroll
+    for (int dt = 0; dt < C::DT; ++dt) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int d = 32 * dt + 8 * g + 4 * h;
+        u32x2 w;
+        w[0] = (uint32_t)f32_to_bf16_bits(acc[dt][4 * g + 0] * inv) |
+               ((uint32_t)f32_to_bf16_bits(acc[dt][4 * g + 1] * inv) << 16);
+        w[1] = (uint32_t)f32_to_bf16_bits(acc[dt][4 * g + 2] * inv) |
+               ((uint32_t)f32_to_bf16_bits(acc[dt][4 * g + 3] * inv) << 16);
+        *reinterpret_cast<u32x2*>(orow + d) = w;
+      }
+    }
+    if (h == 0) a.lse[qtok] = (m_run + __log2f(lt)) * kLn2;
+  }
+}
+
+template <int D, bool FP8>
+hipError_t launch_d(const AttnArgs& a, hipStream_t st) {
+  const int npairs = (a.Nb + 1) / 2;
+  const dim3 grid((unsigned)(a.BH * npairs));
+  if (a.sparse)
+    hipLaunchKernelGGL((attn_kernel<D, true, FP8>), grid, dim3(kThreads), 0, st, a);
+  else
+    hipLaunchKernelGGL((attn_kernel<D, false, FP8>), grid, dim3(kThreads), 0, st, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_attn_mfma(const AttnArgs& a, hipStream_t st) {
+  if (a.BH == 0 || a.N == 0) return hipSuccess;
+  const bool fp8 = a.qk_elt == ELT_FP8;
+  if (a.D == 64) return fp8 ? launch_d<64, true>(a, st) : launch_d<64, false>(a, st);
+  return fp8 ? launch_d<128, true>(a, st) : launch_d<128, false>(a, st);
+}
+
+}  // namespace sa

@@ -1,0 +1,215 @@
+// Step "pool": block means of Q, K, V (the operands of the pooled routing
+// score and of the skipped-block correction), plus V regrouped per 64-key
+// block for the attention kernels.
+//
+// The Sol-Attn project page (section "Abstract") routes on a pooled score;
+// this library reads "pooled" as the mean over each 64-token block's actual
+// tokens.  The kernel is HBM-bound: it reads Q, K and V once (each workgroup
+// one 64-token block of one head, all three tensors in flight together) and
+// writes 1/16 as many bytes of means plus the regrouped V.
+//
+// Every sum is taken in one fixed order (per-thread sequential over rows,
+// then the partial sums of the row groups in order), so the means, and all
+// routing decisions made from them, are bitwise reproducible.
+#include "sa_device.h"
+#include "sa_kernels.h"
+
+namespace sa {
+namespace {
+
+template <int E>
+struct EltBytes;
+template <>
+struct EltBytes<ELT_F32> { static constexpr int v = 4; };
+template <>
+struct EltBytes<ELT_BF16> { static constexpr int v = 2; };
+template <>
+struct EltBytes<ELT_FP8> { static constexpr int v = 1; };
+
+// A 64-token block read as 16-byte chunks by 256 threads: thread t owns
+// chunk column c = t % CPR of rows g, g + G, ... with g = t / CPR.
+template <int E, int D>
+struct Tiling {
+  static constexpr int B = EltBytes<E>::v;
+  static constexpr int EPC = 16 / B;      // elements per chunk
+  static constexpr int CPR = D * B / 16;  // chunks per row
+  static constexpr int G = 256 / CPR;     // row groups
+  static constexpr int P = kBlock / G;    // chunks per thread
+};
+
+template <int E>
+__device__ __forceinline__ void unpack(const u32x4& c, float* out) {
+  if constexpr (E == ELT_F32) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) out[i] = __uint_as_float(c[i]);
+  } else if constexpr (E == ELT_BF16) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      out[2 * i] = __uint_as_float(c[i] << 16);
+      out[2 * i + 1] = __uint_as_float(c[i] & 0xFFFF0000u);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) out[4 * i + j] = fp8e4m3_to_f32((c[i] >> (8 * j)) & 0xFFu);
+  }
+}
+
+template <int E, int D>
+__device__ __forceinline__ void load_block(const uint8_t* __restrict__ base, int nrows,
+                                           u32x4 (&raw)[Tiling<E, D>::P]) {
+  using T = Tiling<E, D>;
+  const int c = threadIdx.x % T::CPR, g = threadIdx.x / T::CPR;
+#pragma unroll
+  for (int i = 0; i < T::P; ++i) {
+    const int r = g + T::G * i;
+    raw[i] = u32x4{0u, 0u, 0u, 0u};
+    if (r < nrows) raw[i] = *reinterpret_cast<const u32x4*>(base + ((size_t)r * D * T::B) + c * 16);
+  }
+}
+
+// mean over rows -> out[0..D) (fp32), scaled by mult; uses part[G][D] in LDS.
+template <int E, int D>
+__device__ __forceinline__ void block_mean(const u32x4 (&raw)[Tiling<E, D>::P], int nrows,
+                                           float mult, float* __restrict__ part,
+                                           float* __restrict__ out_f32,
+                                           uint16_t* __restrict__ out_bf16) {
+  using T = Tiling<E, D>;
+  const int c = threadIdx.x % T::CPR, g = threadIdx.x / T::CPR;
+  float acc[T::EPC];
+#pragma unroll
+  for (int e = 0; e < T::EPC; ++e) acc[e] = 0.f;
+#pragma unroll
+  for (int i = 0; i < T::P; ++i) {
+    float x[T::EPC];
+    unpack<E>(raw[i], x);
+#pragma unroll
+    for (int e = 0; e < T::EPC; ++e) acc[e] += x[e];
+  }
+#pragma unroll
+  for (int e = 0; e < T::EPC; ++e) part[g * D + c * T::EPC + e] = acc[e];
+  __syncthreads();
+  if (threadIdx.x < D) {
+    const int d = threadIdx.x;
+    float s = 0.f;
+#pragma unroll
+    for (int gg = 0; gg < T::G; ++gg) s += part[gg * D + d];
+    const float m = (s / (float)nrows) * mult;
+    out_f32[d] = m;
+    if (out_bf16) out_bf16[d] = f32_to_bf16_bits(m);
+  }
+  __syncthreads();
+}
+
+template <int QE, int VE, int D, bool VT_ONLY>
+__global__ __launch_bounds__(256) void pool_kernel(PoolArgs a) {
+  const int J = blockIdx.x;
+  const int bh = blockIdx.y;
+  const int row0 = J * kBlock;
+  const int nrows = min(kBlock, a.N - row0);
+  const size_t tok0 = (size_t)bh * a.N + row0;
+
+  __shared__ float part[4096];  // up to 64 row groups x 64 dims or 32 x 128
+  __shared__ __attribute__((aligned(16))) uint16_t vtl[D * kBlock];
+
+  using TQ = Tiling<QE, D>;
+  using TV = Tiling<VE, D>;
+  u32x4 rq[TQ::P], rk[TQ::P], rv[TV::P];
+  if constexpr (!VT_ONLY) {
+    load_block<QE, D>(reinterpret_cast<const uint8_t*>(a.q) + tok0 * D * TQ::B, nrows, rq);
+    load_block<QE, D>(reinterpret_cast<const uint8_t*>(a.k) + tok0 * D * TQ::B, nrows, rk);
+  }
+  load_block<VE, D>(reinterpret_cast<const uint8_t*>(a.v) + tok0 * D * TV::B, nrows, rv);
+
+  const size_t mrow = ((size_t)bh * a.Nb + J) * D;
+  if constexpr (!VT_ONLY) {
+    float qm = 1.f, km = 1.f;
+    if constexpr (QE == ELT_FP8) {
+      qm = a.q_scale[(size_t)bh * a.Nb + J];
+      km = a.k_scale[(size_t)bh * a.Nb + J];
+    }
+    block_mean<QE, D>(rq, nrows, qm, part, a.qbar + mrow, nullptr);
+    uint16_t* k16 = (VE == ELT_BF16) ? a.kbar16 + ((size_t)bh * a.Nbp + J) * D : nullptr;
+    block_mean<QE, D>(rk, nrows, km, part, a.kbar + mrow, k16);
+    block_mean<VE, D>(rv, nrows, 1.f, part, a.vbar + mrow, nullptr);
+  }
+
+  if constexpr (VE == ELT_BF16) {
+    // V^T of this block into LDS: element (d, r) at row d, 16-byte chunk
+    // (r/8) ^ ((d/8) & 7), slot r % 8 (rows are 64 keys = 128 bytes).
+    const int c = threadIdx.x % TV::CPR, g = threadIdx.x / TV::CPR;
+#pragma unroll
+    for (int i = 0; i < TV::P; ++i) {
+      const int r = g + TV::G * i;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int d = c * 8 + e;
+        const uint32_t word = rv[i][e >> 1];
+        const uint16_t val = (e & 1) ? (uint16_t)(word >> 16) : (uint16_t)(word & 0xFFFFu);
+        const int pc = (r >> 3) ^ ((d >> 3) & 7);
+        vtl[d * kBlock + pc * 8 + (r & 7)] = val;
+      }
+    }
+    __syncthreads();
+    uint8_t* dst = reinterpret_cast<uint8_t*>(a.vt16 + ((size_t)bh * a.Nb + J) * D * kBlock);
+    constexpr int NCH = D * kBlock * 2 / 16;  // 16-byte chunks in the tile
+#pragma unroll
+    for (int x = threadIdx.x; x < NCH; x += 256) {
+      const int d = x >> 3, cc = x & 7;
+      const int pc = cc ^ ((d >> 3) & 7);
+      *reinterpret_cast<u32x4*>(dst + (size_t)x * 16) =
+          *reinterpret_cast<const u32x4*>(&vtl[d * kBlock + pc * 8]);
+    }
+    if constexpr (!VT_ONLY) {
+      // bf16(vbar) into the transposed groups of 64 blocks.
+      if (threadIdx.x < D) {
+        const int d = threadIdx.x;
+        const size_t grp = (size_t)bh * (a.Nbp / 64) + (J >> 6);
+        a.vbarT16[(grp * D + d) * 64 + (J & 63)] = f32_to_bf16_bits(a.vbar[mrow + d]);
+      }
+      // the last block of a head zero-fills the padding up to Nbp
+      if (J == a.Nb - 1) {
+        for (int JJ = a.Nb; JJ < a.Nbp; ++JJ) {
+          if (threadIdx.x < D) {
+            const int d = threadIdx.x;
+            a.kbar16[((size_t)bh * a.Nbp + JJ) * D + d] = 0;
+            const size_t grp = (size_t)bh * (a.Nbp / 64) + (JJ >> 6);
+            a.vbarT16[(grp * D + d) * 64 + (JJ & 63)] = 0;
+          }
+        }
+      }
+    }
+  }
+}
+
+template <int QE, int VE, int D>
+hipError_t launch_t(const PoolArgs& a, hipStream_t st) {
+  dim3 grid(a.Nb, a.BH);
+  if (a.vt_only) {
+    if constexpr (VE == ELT_BF16) {
+      hipLaunchKernelGGL((pool_kernel<QE, VE, D, true>), grid, dim3(256), 0, st, a);
+    } else {
+      return hipSuccess;
+    }
+  } else {
+    hipLaunchKernelGGL((pool_kernel<QE, VE, D, false>), grid, dim3(256), 0, st, a);
+  }
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_d(const PoolArgs& a, hipStream_t st) {
+  if (a.qk_elt == ELT_F32) return launch_t<ELT_F32, ELT_F32, D>(a, st);
+  if (a.qk_elt == ELT_BF16) return launch_t<ELT_BF16, ELT_BF16, D>(a, st);
+  return launch_t<ELT_FP8, ELT_BF16, D>(a, st);
+}
+
+}  // namespace
+
+hipError_t launch_pool(const PoolArgs& a, hipStream_t st) {
+  if (a.BH == 0 || a.N == 0) return hipSuccess;
+  return a.D == 64 ? launch_d<64>(a, st) : launch_d<128>(a, st);
+}
+
+}  // namespace sa

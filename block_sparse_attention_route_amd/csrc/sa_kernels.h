@@ -1,0 +1,66 @@
+// Host-side launchers of the libsa_route kernels (internal; the public ABI
+// is include/sa_route.h).  Arguments are validated by the caller.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sa {
+
+enum Elt : int { ELT_F32 = 0, ELT_BF16 = 1, ELT_FP8 = 2 };
+
+struct PoolArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const float* q_scale;  // [BH][Nb] (fp8 only)
+  const float* k_scale;
+  int BH, N, Nb, Nbp, D;
+  int qk_elt, v_elt;
+  bool vt_only;          // dense path: only regroup V
+  float* qbar;
+  float* kbar;
+  float* vbar;
+  uint16_t* kbar16;
+  uint16_t* vbarT16;
+  uint16_t* vt16;
+};
+
+struct RouteArgs {
+  const float* qbar;
+  const float* kbar;
+  int BH, Nb, D;
+  float scale, tau;
+  uint8_t* mask;         // [BH][Nb][Nb]
+  int32_t* kept;         // [BH][Nb] or null
+};
+
+struct AttnArgs {
+  const void* q;
+  const void* k;
+  const void* v;         // original V (fp32 path)
+  const float* q_scale;
+  const float* k_scale;
+  const float* qbar;
+  const float* kbar;
+  const float* vbar;
+  const uint16_t* kbar16;
+  const uint16_t* vbarT16;
+  const uint16_t* vt16;
+  void* o;
+  float* lse;
+  int32_t* kept;
+  int BH, N, Nb, Nbp, D;
+  int qk_elt, v_elt;
+  float scale;           // softmax scale s
+  float tau;
+  int correction;
+  bool sparse;           // false: dense attention over all blocks
+};
+
+hipError_t launch_pool(const PoolArgs& a, hipStream_t st);
+hipError_t launch_route(const RouteArgs& a, hipStream_t st);
+hipError_t launch_attn_mfma(const AttnArgs& a, hipStream_t st);
+hipError_t launch_attn_f32(const AttnArgs& a, hipStream_t st);
+
+}  // namespace sa

@@ -20,7 +20,8 @@ spawned into four streams (Q, K, V, scaling):
   axis may use a smaller maximum), phi_s ~ U[0, 2*pi), a_s and eps ~ N(0, 1)
   per feature;
 * Q and K are both multiplied by c = sqrt(3 / std(q_i.k_j / sqrt(D))) over
-  65,536 random pairs, which sets the per-head logit std to about 3;
+  65,536 random pairs, which sets the per-head logit std to about 3 (c = 1
+  when that std is below 1e-6, e.g. a single-token grid);
 * optional sink tokens: rows 0..n_sink-1 of Q and K rescaled to 4x the mean
   row norm of their tensor (after the scaling);
 * V ~ N(0, 1);
@@ -132,7 +133,9 @@ def _head(wl: Workload, b: int, h: int, u: np.ndarray):
     i = rs.integers(0, wl.N, size=65536)
     j = rs.integers(0, wl.N, size=65536)
     logit = np.einsum("nd,nd->n", q[i].astype(np.float64), k[j].astype(np.float64)) / math.sqrt(wl.D)
-    c = np.float32(math.sqrt(3.0 / max(logit.std(), 1e-12)))
+    sd = logit.std()
+    # a grid of one token (or identical tokens) has no logit spread to normalise
+    c = np.float32(math.sqrt(3.0 / sd) if sd > 1e-6 else 1.0)
     q *= c
     k *= c
     for x in (q, k):

@@ -1,0 +1,173 @@
+/*
+ * sa_route.h -- C ABI of the on-the-fly block-sparse self-attention library
+ * for AMD Instinct MI355X (gfx950).  Library: libsa_route.so.
+ *
+ * Operation (Sol-Attn project page, nvlabs.github.io/Sana/Sol-Attn, section
+ * "Abstract"; Sol-Engine README, section "Sol-Attention"): video-token
+ * self-attention in which every query block is routed, by a query-dependent
+ * threshold on a pooled score computed on chip, to the key blocks it attends
+ * exactly; the skipped blocks are not dropped but enter through a cheap
+ * correction; routing, sparse compute and correction share one online-softmax
+ * pass.  The concrete reading implemented here, per (batch b, head h), with
+ * block size beta = 64, Nb = ceil(N / 64), block J = tokens
+ * [64J, min(64J + 64, N)) of size n_J, and s = scale (1/sqrt(D) by default):
+ *
+ *   pool     qbar_I, kbar_J, vbar_J = means over the tokens of each block
+ *   route    p_IJ = s * qbar_I . kbar_J ;  keep_IJ = p_IJ >= max_J p_IJ - tau
+ *   exact    logits s * q_i . k_j for the tokens j of kept blocks
+ *   correct  each skipped J acts as n_J copies of (kbar_J, vbar_J): logit
+ *            s * q_i . kbar_J with weight n_J (only if correction != 0)
+ *   output   o_i = softmax-weighted sum of values over all those logits,
+ *            lse_i = natural-log log-sum-exp of the weighted logits.
+ *
+ * tau = +INFINITY keeps every block: plain dense softmax attention.
+ *
+ * Conventions for every entry point:
+ *  - Tensors are row-major and contiguous.  Q, K, V, O are [B, H, N, D];
+ *    LSE is [B, H, N] float32; fp8 block scales are [B, H, Nb] float32;
+ *    masks are [B, H, Nb, Nb] uint8 (0/1); kept counts are [B, H, Nb] int32.
+ *  - Pointers to tensors and the workspace are DEVICE pointers, owned by the
+ *    caller; shape/params/inputs structs are HOST pointers, read during the
+ *    call only.  The library allocates no memory and keeps no per-call state.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *    Calls only enqueue work and return; they never synchronise.
+ *  - All arguments are validated on the host before anything is enqueued.
+ *    On any error the call returns a nonzero sa_status and enqueues nothing;
+ *    sa_last_error() then describes the failure (per calling thread).  A
+ *    failed kernel launch returns SA_ERR_HIP.  No C++ exception crosses the ABI.
+ *  - Outputs must not alias inputs or the workspace; they are fully
+ *    overwritten.  Calls on different streams need distinct workspaces.
+ *  - A call with B*H*N == 0 is valid, touches no pointer and returns SA_OK.
+ *  - Results are bitwise deterministic for fixed inputs on a given device.
+ *  - Supported: D in {64, 128}; block = 64; N <= SA_MAX_N; dtype pairs
+ *    (qk, v) in {(F32, F32), (BF16, BF16), (FP8_E4M3, BF16)}.
+ *  - Alignment: q, k, v, o and the workspace 16 bytes; lse, kept, scales 4.
+ */
+#ifndef SA_ROUTE_H
+#define SA_ROUTE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SA_ABI_VERSION 1
+#define SA_BLOCK 64
+#define SA_MAX_NB 4096
+#define SA_MAX_N (SA_BLOCK * SA_MAX_NB)
+
+typedef enum sa_status {
+  SA_OK = 0,
+  SA_ERR_NULL = 1,        /* a required pointer is NULL */
+  SA_ERR_SHAPE = 2,       /* bad B/H/N/D, N != T*Hg*Wg, or N > SA_MAX_N */
+  SA_ERR_PARAM = 3,       /* block != 64, tau < 0 or NaN, bad correction flag, bad scale */
+  SA_ERR_DTYPE = 4,       /* unsupported (qk_dtype, v_dtype) pair or scales given/missing */
+  SA_ERR_ALIGN = 5,       /* pointer misaligned */
+  SA_ERR_WORKSPACE = 6,   /* workspace smaller than sa_workspace_bytes() */
+  SA_ERR_UNSUPPORTED = 7, /* valid request this build does not implement */
+  SA_ERR_HIP = 8          /* a HIP runtime call or kernel launch failed */
+} sa_status;
+
+typedef enum sa_dtype {
+  SA_F32 = 0,
+  SA_BF16 = 1,
+  SA_FP8_E4M3 = 2         /* OCP e4m3fn (max 448), with one fp32 scale per 64-token block */
+} sa_dtype;
+
+/* Q/K/V shape and the video token grid.  Tokens are in frame-major raster
+ * order, token n = (t*Hg + y)*Wg + x; N must equal T*Hg*Wg.  Blocks are 64
+ * consecutive tokens of this order (Sol-Engine README, "Sol-Attention":
+ * the replaced operator is video-token self-attention). */
+typedef struct sa_shape {
+  int32_t B, H, N, D;
+  int32_t T, Hg, Wg;
+} sa_shape;
+
+/* Routing parameters (Sol-Attn page, "Abstract": query-dependent threshold).
+ * block: must be 64.  tau: threshold below the row maximum of the proxy, in
+ * scaled-logit (natural log) units; tau >= 0, +INFINITY keeps every block.
+ * correction: 1 = add the skipped-block correction, 0 = drop skipped blocks.
+ * scale: softmax scale s; <= 0 selects 1/sqrt(D); must be finite. */
+typedef struct sa_params {
+  int32_t block;
+  float tau;
+  int32_t correction;
+  float scale;
+} sa_params;
+
+/* Input tensors.  q_scale/k_scale: [B, H, Nb] fp32 block scales, required
+ * iff qk_dtype == SA_FP8_E4M3 (element value = code * scale of its block),
+ * otherwise must be NULL.  qk_dtype / v_dtype are sa_dtype values. */
+typedef struct sa_inputs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const float* q_scale;
+  const float* k_scale;
+  int32_t qk_dtype;
+  int32_t v_dtype;
+} sa_inputs;
+
+/* ABI version of the loaded library (SA_ABI_VERSION it was built with). */
+int32_t sa_abi_version(void);
+
+/* Human-readable name of a status code (static string). */
+const char* sa_status_string(sa_status s);
+
+/* Detail of the last failed call made by this thread (static per thread;
+ * empty string if none). */
+const char* sa_last_error(void);
+
+/* Workspace bytes that sa_pool / sa_route / sa_forward / sa_forward_pooled
+ * need for this shape and dtypes (block means in fp32, bf16 copies of the
+ * key/value means, and V regrouped per 64-key block).  Returns 0 if the
+ * arguments are invalid.  Pass params = NULL for the default params. */
+size_t sa_workspace_bytes(const sa_shape* shape, const sa_params* params, const sa_inputs* in);
+
+/* Step "pool" (the pooled score's operands): writes qbar, kbar, vbar (fp32
+ * means over each block's actual n_J tokens; fp8 inputs are dequantised with
+ * their block scale) and the regrouped V used by the attention kernels into
+ * the workspace. */
+sa_status sa_pool(const sa_shape* shape, const sa_params* params, const sa_inputs* in,
+                  void* ws, size_t ws_bytes, void* stream);
+
+/* Steps "pool" + "route", standalone, for inspection and tests: writes the
+ * 0/1 keep mask [B, H, Nb, Nb] (mask[b][h][I][J] = 1 iff query block I keeps
+ * key block J) and, if kept != NULL, the kept count per query block
+ * [B, H, Nb].  Uses the same device routine, in the same float32 order, as
+ * sa_forward, so the two agree bit for bit. */
+sa_status sa_route(const sa_shape* shape, const sa_params* params, const sa_inputs* in,
+                   uint8_t* mask, int32_t* kept, void* ws, size_t ws_bytes, void* stream);
+
+/* The fused path: pool, then one kernel that per query block computes the
+ * proxy row on chip (never written out), thresholds it, folds the correction
+ * of the skipped blocks into the running softmax max/sum, and runs exact
+ * flash attention over the kept blocks.  Writes O ([B, H, N, D], dtype =
+ * v_dtype) and LSE ([B, H, N] fp32, natural log, including correction mass);
+ * kept (optional, [B, H, Nb] int32) receives each query block's kept count. */
+sa_status sa_forward(const sa_shape* shape, const sa_params* params, const sa_inputs* in,
+                     void* o, float* lse, int32_t* kept, void* ws, size_t ws_bytes, void* stream);
+
+/* sa_forward without the pool step: the workspace must already hold the
+ * output of sa_pool for the same inputs, shape and params. */
+sa_status sa_forward_pooled(const sa_shape* shape, const sa_params* params, const sa_inputs* in,
+                            void* o, float* lse, int32_t* kept, void* ws, size_t ws_bytes,
+                            void* stream);
+
+/* Workspace bytes for sa_dense_forward (0 on invalid arguments). */
+size_t sa_dense_workspace_bytes(const sa_shape* shape, const sa_inputs* in);
+
+/* Dense bidirectional softmax attention, the "Dense" baseline of the Sol-Attn
+ * page and the tau = +INFINITY limit of sa_forward: O and LSE as above.
+ * scale <= 0 selects 1/sqrt(D).  For bf16 V the workspace receives V
+ * regrouped per 64-key block; for fp32 it may be NULL (size 0). */
+sa_status sa_dense_forward(const sa_shape* shape, float scale, const sa_inputs* in,
+                           void* o, float* lse, void* ws, size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SA_ROUTE_H */

@@ -1,0 +1,102 @@
+"""Parity helpers: HIP results against the CPU oracle on the same seeded inputs.
+
+Tolerances (fixed by the method's stated bars):
+* float32 path: row-normwise relative error of O <= 1e-5
+  (max_i |o_i - ref_i|_inf / |ref_i|_inf) and |LSE - ref| <= 1e-5 * max(1, |ref|);
+* bf16 path: max |O - ref| <= 2e-2 and mean |O - ref| <= 2e-3 against the
+  float64 oracle on the same bf16-rounded inputs;
+* fp8 Q/K path: max |O - ref| <= 4e-2 against the oracle on the dequantised
+  inputs;
+* masks: bit-exact except blocks whose float64 proxy lies within 1e-3 of the
+  threshold (those are counted); outputs are then compared with the oracle
+  evaluated on the GPU's mask.
+LSE of the bf16/fp8 paths: its error comes only from float32 accumulation of
+exact bf16/fp8 products and from the exp2/log2 approximations, far below the
+bf16 output rounding; it is bounded here by 1e-2 absolute.
+"""
+from __future__ import annotations
+
+import math
+import sys
+
+import numpy as np
+import torch
+
+from oracle import attention as orc
+
+BAND = 1e-3
+TOL = {
+    "f32": dict(row_rel=1e-5, lse_rel=1e-5),
+    "bf16": dict(max_abs=2e-2, mean_abs=2e-3, lse_abs=1e-2),
+    "fp8": dict(max_abs=4e-2, lse_abs=2e-2),
+}
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def to_gpu(inp):
+    dev = torch.device("cuda:0")
+    g = lambda t: None if t is None else t.to(dev).contiguous()  # noqa: E731
+    return g(inp.q), g(inp.k), g(inp.v), g(inp.q_scale), g(inp.k_scale)
+
+
+def grid_of(wl):
+    return (wl.T, wl.Hg, wl.Wg)
+
+
+def mask_check(inp, b, h, gpu_mask: np.ndarray, tau: float, scale=None):
+    """Compare the GPU keep mask of one head with the float64 routing.
+
+    Returns (keep_for_oracle, n_band, n_flipped_in_band); asserts that no block
+    outside the near-threshold band differs."""
+    q, k, _ = inp.head64(b, h)
+    keep, p, m = orc.route(q, k, inp.wl.block, tau, scale)
+    gm = gpu_mask.astype(bool)
+    if math.isinf(tau):
+        band = np.zeros_like(keep)
+    else:
+        band = np.abs(p - (m - tau)[:, None]) < BAND
+    diff = gm != keep
+    outside = diff & ~band
+    assert not outside.any(), (
+        f"head ({b},{h}): {int(outside.sum())} mask entries differ outside the {BAND} band, "
+        f"first at {np.argwhere(outside)[0].tolist()}")
+    return gm, int(band.sum()), int((diff & band).sum())
+
+
+def output_check(inp, b, h, o_gpu: torch.Tensor, lse_gpu: torch.Tensor, keep: np.ndarray, tau: float,
+                 correction: bool, qblocks=None, scale=None, dense=False):
+    """Oracle output for the given query blocks of head (b, h) against the GPU's."""
+    wl = inp.wl
+    q, k, v = inp.head64(b, h)
+    N = q.shape[0]
+    ranges = orc.block_ranges(N, wl.block)
+    qblocks = list(range(len(ranges))) if qblocks is None else sorted(set(qblocks))
+    rows = np.concatenate([np.arange(*ranges[I]) for I in qblocks])
+    if dense:
+        o_ref, lse_ref = orc.dense_head(q, k, v, scale, rows=rows)
+    else:
+        o_full, lse_full, _ = orc.forward_head(q, k, v, wl.block, tau, correction, scale, keep=keep,
+                                               qblocks=qblocks)
+        o_ref, lse_ref = o_full[rows], lse_full[rows]
+    o = o_gpu[b, h].float().cpu().numpy().astype(np.float64)[rows]
+    lse = lse_gpu[b, h].cpu().numpy().astype(np.float64)[rows]
+    assert np.isfinite(o).all() and np.isfinite(lse).all(), "non-finite GPU output"
+    err = np.abs(o - o_ref)
+    lerr = np.abs(lse - lse_ref)
+    t = TOL[wl.dtype]
+    stats = dict(max_abs=float(err.max()), mean_abs=float(err.mean()), lse_abs=float(lerr.max()))
+    if wl.dtype == "f32":
+        row_rel = (err.max(axis=1) / np.maximum(np.abs(o_ref).max(axis=1), 1e-30)).max()
+        stats["row_rel"] = float(row_rel)
+        assert row_rel <= t["row_rel"], stats
+        assert (lerr <= t["lse_rel"] * np.maximum(1.0, np.abs(lse_ref))).all(), stats
+    else:
+        assert stats["max_abs"] <= t["max_abs"], stats
+        if "mean_abs" in t:
+            assert stats["mean_abs"] <= t["mean_abs"], stats
+        assert stats["lse_abs"] <= t["lse_abs"], stats
+    return stats

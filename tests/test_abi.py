@@ -1,0 +1,154 @@
+"""The C ABI library loads, exports every declared entry point, and validates
+arguments on the host (CPU only: no call here reaches a HIP API, since every
+case fails validation, is empty, or only sizes a workspace)."""
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+from block_sparse_attention_route_amd import api
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sa_route.h")
+
+FAKE = 1 << 20   # stands in for an aligned device pointer; never dereferenced on failure paths
+
+
+def _declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(sa_[a-z_]+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return api.load_library()
+
+
+def test_exports_every_declared_symbol(lib):
+    names = _declared_functions()
+    assert len(names) >= 9
+    for n in names:
+        assert hasattr(lib, n), f"{n} declared in sa_route.h but not exported"
+
+
+def test_abi_version(lib):
+    assert api.sa_abi_version() == 1
+
+
+def test_status_strings(lib):
+    for code, name in enumerate(api.STATUS):
+        assert lib.sa_status_string(code).decode().startswith(name)
+
+
+def _shape(B=1, H=2, T=2, Hg=8, Wg=9, D=128, N=None):
+    N = T * Hg * Wg if N is None else N
+    return api.Shape(B, H, N, D, T, Hg, Wg)
+
+
+def _inputs(qk=api.SA_BF16, v=api.SA_BF16, q=FAKE, k=FAKE, vv=FAKE, qs=None, ks=None):
+    return api.Inputs(q, k, vv, qs, ks, qk, v)
+
+
+def _params(block=64, tau=2.0, corr=1, scale=0.0):
+    return api.Params(block, tau, corr, scale)
+
+
+def _fwd(lib, sh, pr, inp, o=FAKE, lse=FAKE, kept=None, ws=FAKE, ws_bytes=1 << 40):
+    return lib.sa_forward(ctypes.byref(sh), ctypes.byref(pr), ctypes.byref(inp), o, lse, kept, ws, ws_bytes, None)
+
+
+def test_workspace_bytes_layout(lib):
+    sh = _shape(B=1, H=3, T=1, Hg=10, Wg=13, D=128)     # N = 130 -> Nb = 3, Nbp = 64
+    n = lib.sa_workspace_bytes(ctypes.byref(sh), None, ctypes.byref(_inputs()))
+    BH, Nb, Nbp, D = 3, 3, 64, 128
+
+    def a256(x):
+        return (x + 255) // 256 * 256
+    expect = 3 * a256(BH * Nb * D * 4) + 2 * a256(BH * Nbp * D * 2) + a256(BH * Nb * D * 64 * 2)
+    assert n == expect
+    # fp32 path keeps only the fp32 means
+    n32 = lib.sa_workspace_bytes(ctypes.byref(sh), None, ctypes.byref(_inputs(api.SA_F32, api.SA_F32)))
+    assert n32 == 3 * a256(BH * Nb * D * 4)
+    nd = lib.sa_dense_workspace_bytes(ctypes.byref(sh), ctypes.byref(_inputs()))
+    assert nd == a256(BH * Nb * D * 64 * 2)
+    nd32 = lib.sa_dense_workspace_bytes(ctypes.byref(sh), ctypes.byref(_inputs(api.SA_F32, api.SA_F32)))
+    assert nd32 == 0
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(D=96), "SA_ERR_SHAPE"),
+    (dict(N=100), "SA_ERR_SHAPE"),               # N != T*Hg*Wg
+    (dict(T=65, Hg=64, Wg=64), "SA_ERR_SHAPE"),  # N > SA_MAX_N
+    (dict(B=-1), "SA_ERR_SHAPE"),
+])
+def test_bad_shapes(lib, kw, code):
+    sh = _shape(**kw)
+    assert api.status_name(_fwd(lib, sh, _params(), _inputs())) == code
+    assert lib.sa_last_error().decode()
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(block=32), "SA_ERR_PARAM"),
+    (dict(tau=-1.0), "SA_ERR_PARAM"),
+    (dict(tau=math.nan), "SA_ERR_PARAM"),
+    (dict(corr=2), "SA_ERR_PARAM"),
+    (dict(scale=math.inf), "SA_ERR_PARAM"),
+])
+def test_bad_params(lib, kw, code):
+    assert api.status_name(_fwd(lib, _shape(), _params(**kw), _inputs())) == code
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(qk=api.SA_BF16, v=api.SA_F32), "SA_ERR_DTYPE"),
+    (dict(qk=api.SA_F32, v=api.SA_BF16), "SA_ERR_DTYPE"),
+    (dict(qk=api.SA_FP8_E4M3, v=api.SA_F32), "SA_ERR_DTYPE"),
+    (dict(qk=7, v=api.SA_BF16), "SA_ERR_DTYPE"),
+    (dict(qk=api.SA_FP8_E4M3, v=api.SA_BF16), "SA_ERR_DTYPE"),            # fp8 without scales
+    (dict(qk=api.SA_BF16, v=api.SA_BF16, qs=FAKE, ks=FAKE), "SA_ERR_DTYPE"),  # scales for bf16
+    (dict(q=None), "SA_ERR_NULL"),
+    (dict(vv=None), "SA_ERR_NULL"),
+    (dict(k=FAKE + 8), "SA_ERR_ALIGN"),
+])
+def test_bad_inputs(lib, kw, code):
+    assert api.status_name(_fwd(lib, _shape(), _params(), _inputs(**kw))) == code
+
+
+def test_bad_outputs_and_workspace(lib):
+    sh, pr, inp = _shape(), _params(), _inputs()
+    assert api.status_name(_fwd(lib, sh, pr, inp, o=None)) == "SA_ERR_NULL"
+    assert api.status_name(_fwd(lib, sh, pr, inp, lse=None)) == "SA_ERR_NULL"
+    assert api.status_name(_fwd(lib, sh, pr, inp, o=FAKE + 4)) == "SA_ERR_ALIGN"
+    assert api.status_name(_fwd(lib, sh, pr, inp, kept=FAKE + 2)) == "SA_ERR_ALIGN"
+    need = lib.sa_workspace_bytes(ctypes.byref(sh), None, ctypes.byref(inp))
+    assert api.status_name(_fwd(lib, sh, pr, inp, ws_bytes=need - 1)) == "SA_ERR_WORKSPACE"
+    assert api.status_name(_fwd(lib, sh, pr, inp, ws=None)) == "SA_ERR_NULL"
+    assert api.status_name(_fwd(lib, sh, pr, inp, ws=FAKE + 8)) == "SA_ERR_ALIGN"
+    # params pointer required by the compute entry points
+    st = lib.sa_forward(ctypes.byref(sh), None, ctypes.byref(inp), FAKE, FAKE, None, FAKE, 1 << 40, None)
+    assert api.status_name(st) == "SA_ERR_NULL"
+
+
+def test_route_and_dense_validation(lib):
+    sh, pr, inp = _shape(), _params(), _inputs()
+    st = lib.sa_route(ctypes.byref(sh), ctypes.byref(pr), ctypes.byref(inp), None, None, FAKE, 1 << 40, None)
+    assert api.status_name(st) == "SA_ERR_NULL"
+    st = lib.sa_dense_forward(ctypes.byref(sh), math.nan, ctypes.byref(inp), FAKE, FAKE, FAKE, 1 << 40, None)
+    assert api.status_name(st) == "SA_ERR_PARAM"
+    st = lib.sa_dense_forward(ctypes.byref(_shape(D=32)), 0.0, ctypes.byref(inp), FAKE, FAKE, FAKE, 1 << 40, None)
+    assert api.status_name(st) == "SA_ERR_SHAPE"
+    st = lib.sa_pool(ctypes.byref(sh), ctypes.byref(_params(tau=-2.0)), ctypes.byref(inp), FAKE, 1 << 40, None)
+    assert api.status_name(st) == "SA_ERR_PARAM"
+
+
+@pytest.mark.parametrize("kw", [dict(B=0), dict(H=0), dict(T=0)])
+def test_empty_calls_are_ok_without_pointers(lib, kw):
+    sh = _shape(**kw)
+    inp = _inputs(q=None, k=None, vv=None)
+    assert _fwd(lib, sh, _params(), inp, o=None, lse=None, ws=None, ws_bytes=0) == 0
+    st = lib.sa_route(ctypes.byref(sh), ctypes.byref(_params()), ctypes.byref(inp), None, None, None, 0, None)
+    assert st == 0
+    st = lib.sa_dense_forward(ctypes.byref(sh), 0.0, ctypes.byref(inp), None, None, None, 0, None)
+    assert st == 0

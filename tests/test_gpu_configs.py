@@ -1,0 +1,59 @@
+"""GPU parity at the five full workload sizes, in the launch configuration the
+benchmark times (sa_pool then the fused kernel over all heads at once).
+
+Masks are compared for every head; O and LSE on sampled outputs the oracle
+computes one query block at a time: heads (0,0), (B-1,H-1) and two seeded
+random heads, each at its first, ragged last and two random query blocks.
+"""
+import math
+from concurrent.futures import ThreadPoolExecutor
+
+import numpy as np
+import pytest
+import torch
+
+from block_sparse_attention_route_amd import api, synth
+from tests.parity import mask_check, output_check, say, to_gpu
+
+pytestmark = pytest.mark.gpu
+
+CASES = [("tiny", 4.0), ("480p", 4.0), ("720p", 2.0), ("720p", 4.0), ("720p", 8.0), ("1080p", 4.0),
+         ("720p_cfg_fp8", 4.0)]
+
+
+@pytest.mark.parametrize("name,tau", CASES, ids=[f"{n}-tau{t:g}" for n, t in CASES])
+def test_full_size_config(name, tau):
+    wl = synth.workload(name)
+    say(f"case {name} tau={tau}: B{wl.B} H{wl.H} N{wl.N} D{wl.D} {wl.dtype}")
+    inp = synth.generate(wl)
+    q, k, v, qs, ks = to_gpu(inp)
+    grid = (wl.T, wl.Hg, wl.Wg)
+    ws = api.sa_pool(q, k, v, grid, tau=tau, q_scale=qs, k_scale=ks)
+    o, lse, kept = api.sa_forward_pooled(q, k, v, grid, tau=tau, workspace=ws, q_scale=qs, k_scale=ks,
+                                         want_kept=True)
+    mask, kept_r = api.sa_route(q, k, v, grid, tau=tau, q_scale=qs, k_scale=ks)
+    torch.cuda.synchronize()
+    assert torch.equal(kept.cpu(), kept_r.cpu())
+    del ws, q, k, v
+    mask_np = mask.cpu().numpy()
+    del mask
+    heads = [(b, h) for b in range(wl.B) for h in range(wl.H)]
+
+    def one(bh):
+        return mask_check(inp, bh[0], bh[1], mask_np[bh], tau)
+
+    with ThreadPoolExecutor(max_workers=8) as ex:
+        res = list(ex.map(one, heads))
+    band = sum(r[1] for r in res)
+    flipped = sum(r[2] for r in res)
+    say(f"  masks ok for {len(heads)} heads; density {mask_np.mean():.3f}; near-threshold {band}, "
+        f"flipped {flipped}")
+    rng = np.random.default_rng(123)
+    sample = {(0, 0), (wl.B - 1, wl.H - 1)}
+    while len(sample) < min(4, len(heads)):
+        sample.add(heads[int(rng.integers(len(heads)))])
+    for (b, h) in sorted(sample):
+        keep = res[heads.index((b, h))][0]
+        qb = {0, wl.Nb - 1, int(rng.integers(wl.Nb)), int(rng.integers(wl.Nb))}
+        st = output_check(inp, b, h, o, lse, keep, tau, wl.correction, qblocks=qb)
+        say(f"  head ({b},{h}) blocks {sorted(qb)}: {st}")
