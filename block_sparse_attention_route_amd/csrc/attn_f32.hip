@@ -30,20 +30,17 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(AttnArgs a) {
   __shared__ float lw[kBlock];          // log-multiplicity of each staged key
   __shared__ float p[kMaxNb];
   __shared__ uint8_t flags[SPARSE ? kMaxNb : 1];
-  __shared__ float qb[2 * D];
+  __shared__ float qb[D];
   __shared__ float redf[8];
   __shared__ int redi[8];
   __shared__ int counts[2];
 
   if constexpr (SPARSE) {
-    for (int d = lane; d < D; d += 64) {
-      qb[d] = a.qbar[((size_t)bh * Nb + I) * D + d];
-      qb[D + d] = 0.f;
-    }
+    for (int d = lane; d < D; d += 64) qb[d] = a.qbar[((size_t)bh * Nb + I) * D + d];
     __syncthreads();
-    proxy_row_pair<D, 64>(qb, a.kbar + (size_t)bh * Nb * D, Nb, a.scale, false, p);
+    proxy_rows<D, 64, 1>(qb, a.kbar + (size_t)bh * Nb * D, Nb, a.scale, 1, p);
     __syncthreads();
-    threshold_rows<64>(p, Nb, false, a.tau, flags, redf, redi, counts);
+    threshold_rows<64, 1>(p, Nb, 1, a.tau, flags, redf, redi, counts);
     if (a.kept && lane == 0) a.kept[(size_t)bh * Nb + I] = counts[0];
   }
 

@@ -23,19 +23,23 @@
 //      ragged last key block masked;
 //   4. epilogue: O = acc / l in bf16 and the natural-log LSE.
 //
-// Tiling.  256 threads = 4 waves; wave w owns 32 query rows (query block
-// 2*pair + w/2, rows 32*(w%2) ..) against the full 64-key tile.  Products use
-// v_mfma_f32_32x32x16_bf16 with the roles transposed, S^T = K Q^T and
-// O^T = V^T P^T: a lane owns one query column, so the softmax row max and sum
-// are lane-local plus one exchange with lane^32, and the exponentiated scores
-// are already the B operand of the PV product.  The MFMA row order of K is
-// permuted (bits 2 and 3 swapped) so that the keys a lane holds after S^T are
-// exactly the keys its PV operand needs.  K tiles are row-major and V tiles
-// arrive pre-transposed (d-major) from the pool step; both are loaded straight
-// from global memory into double-buffered LDS (global_load_lds_dwordx4), with
-// an XOR swizzle on 16-byte chunks that keeps the MFMA operand reads
-// conflict-free.  Workgroup ids are remapped so each XCD walks a contiguous
-// range of query blocks (shared key blocks stay in that XCD's L2).
+// Tiling.  A workgroup takes QB adjacent query blocks (QB = 4 at D = 128, 2
+// at D = 64) with two waves per block; wave w owns 32 query rows (query block
+// QB*group + w/2, rows 32*(w%2) ..) against the full 64-key tile.  Products
+// use v_mfma_f32_32x32x16_bf16 (v_mfma_f32_32x32x16_fp8_fp8 for fp8 Q K^T)
+// with the roles transposed, S^T = K Q^T and O^T = V^T P^T: a lane owns one
+// query column, so the softmax row max and sum are lane-local plus one
+// exchange with lane^32, and the exponentiated scores are already the B
+// operand of the PV product.  The MFMA row order of K is permuted (bits 2 and
+// 3 swapped) so that the keys a lane holds after S^T are exactly the keys its
+// PV operand needs.  K tiles are row-major and V tiles arrive pre-transposed
+// (d-major) from the pool step; both are copied straight from global memory
+// into a ring of LDS stages (LDS DMA, global_load_lds_dwordx4) issued one
+// tile ahead, with an XOR swizzle on 16-byte chunks that keeps the MFMA
+// operand reads free of bank conflicts.  Workgroup ids are remapped so that
+// each XCD works on a chunk of adjacent query blocks while all XCDs stay on
+// the same head (shared key blocks hit in that XCD's L2, the head's K/V stays
+// in the last-level cache).
 #include "sa_device.h"
 #include "sa_kernels.h"
 
@@ -43,9 +47,6 @@ namespace sa {
 namespace {
 
 constexpr int kThreads = 256;
-
-typedef __attribute__((address_space(3))) void lds_void_t;
-typedef __attribute__((address_space(1))) void gbl_void_t;
 
 // Key row that MFMA row m of a 32-key tile reads: swap bits 2 and 3.
 __device__ __forceinline__ int kperm(int m) { return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1); }
@@ -62,15 +63,10 @@ __device__ __forceinline__ int swz_any(int row, int chunk) {
   }
 }
 
-// 16 bytes from global straight into LDS.  The LDS destination of lane l is
-// lds_wave_base + 16*l; lds_wave_base must be the same for the whole wave.
-__device__ __forceinline__ void g2lds16(const void* gsrc, void* lds_wave_base) {
-  __builtin_amdgcn_global_load_lds((gbl_void_t*)gsrc, (lds_void_t*)lds_wave_base, 16, 0, 0);
-}
-
 template <int NT>
 __device__ __forceinline__ void build_union(const uint8_t* __restrict__ flags, int Nb,
                                             uint16_t* __restrict__ ulist, int* total, int* wsum) {
+  constexpr int NW = NT / 64;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int seg = (Nb + NT - 1) / NT;
   const int j0 = min(Nb, tid * seg), j1 = min(Nb, j0 + seg);
@@ -85,7 +81,8 @@ __device__ __forceinline__ void build_union(const uint8_t* __restrict__ flags, i
   if (lane == 63) wsum[wave] = x;
   __syncthreads();
   int base = 0;
-  for (int w = 0; w < wave; ++w) base += wsum[w];
+#pragma unroll
+  for (int w = 0; w < NW; ++w) base += (w < wave) ? wsum[w] : 0;
   int pos = base + x - cnt;
   for (int j = j0; j < j1; ++j) {
     const int f = flags[j];
@@ -105,57 +102,122 @@ struct Cfg {
   static constexpr int CPR8 = KROW8 / 16;
   static constexpr int KTILE = 64 * KROW16;  // K buffer bytes (sized for bf16)
   static constexpr int VTILE = D * 128;      // V^T tile: D rows of 64 bf16 keys
-  static constexpr int STAGE = 2 * (KTILE + VTILE);
-  static constexpr int PROXY = 2 * kMaxNb * 4;
-  static constexpr int SMEM = STAGE > PROXY ? STAGE : PROXY;
+  static constexpr int STAGE = KTILE + VTILE;
 };
 
-template <int D, bool SPARSE, bool FP8>
-__global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnArgs a) {
+// 16 bytes per lane from global memory straight into LDS (LDS DMA): lane l's
+// bytes land at lds_wave_base + 16*l.  Issued as inline assembly so that the
+// compiler does not order every later LDS read behind the copy; the kernel
+// waits for each tile itself (vmcnt) before the barrier that publishes it.
+__device__ __forceinline__ void dma16(const void* gsrc, uint32_t lds_wave_base) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
+               :
+               : "v"(gsrc), "s"(__builtin_amdgcn_readfirstlane(lds_wave_base))
+               : "memory", "m0");
+}
+
+// One float from a wave-uniform global address through the scalar unit,
+// waited for inside the same statement: a vector load here would make the
+// compiler wait for the in-flight tile copies as well.
+__device__ __forceinline__ float scalar_load_f32(const float* p) {
+  float v;
+  // readfirstlane is a 32-bit operation: make each half of the address uniform
+  const uint64_t u = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)u);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(u >> 32));
+  const uint64_t up = ((uint64_t)hi << 32) | lo;
+  asm volatile("s_load_dword %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(v) : "s"(up) : "memory");
+  return v;
+}
+
+// s_waitcnt vmcnt(n) with the other counters left alone (gfx9 encoding).
+template <int n>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(n >= 0 && n < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+template <int LPT, int MAXAHEAD>
+__device__ __forceinline__ void wait_tiles_ahead(int ahead) {
+  // all but the last ahead*LPT vector-memory loads of this thread complete
+  if constexpr (MAXAHEAD >= 3) {
+    if (ahead >= 3) { wait_vmcnt<3 * LPT>(); return; }
+  }
+  if constexpr (MAXAHEAD >= 2) {
+    if (ahead == 2) { wait_vmcnt<2 * LPT>(); return; }
+  }
+  if constexpr (MAXAHEAD >= 1) {
+    if (ahead == 1) { wait_vmcnt<LPT>(); return; }
+  }
+  wait_vmcnt<0>();
+}
+
+template <int D, bool SPARSE, bool FP8, int QB, int ST>
+__global__ __launch_bounds__(128 * QB, QB == 2 ? 2 : 1) void attn_kernel(AttnArgs a) {
   using C = Cfg<D>;
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[C::SMEM];
+  constexpr int NT = 128 * QB;        // threads
+  constexpr int NW = 2 * QB;          // waves: two 32-row halves per query block
+  constexpr int KI16 = C::KTILE / 1024 / NW;       // per-thread DMA copies, bf16 K tile
+  constexpr int KI8 = C::KTILE / 2 / 1024 / NW;    // fp8 K tile
+  constexpr int VI = C::VTILE / 1024 / NW;         // V^T tile
+  constexpr int LPT = (FP8 ? (KI8 < KI16 ? KI8 : KI16) : KI16) + VI;  // fewest copies per tile
+  constexpr int SMEM_STAGE = ST * C::STAGE;
+  constexpr int SMEM_PROXY = SPARSE ? QB * kMaxNb * 4 : 0;
+  constexpr int SMEM = SMEM_STAGE > SMEM_PROXY ? SMEM_STAGE : SMEM_PROXY;
+  static_assert(KI8 >= 1 && VI >= 1, "tile copies per wave");
+
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[SMEM];
   __shared__ uint8_t flags[SPARSE ? kMaxNb : 1];
   __shared__ uint16_t ulist[SPARSE ? kMaxNb : 1];
-  __shared__ float qb[SPARSE ? 2 * D : 1];
-  __shared__ float redf[8];
-  __shared__ int redi[8];
-  __shared__ int counts[2];
+  __shared__ uint64_t skipbits[SPARSE ? QB * (kMaxNb / 64) : 1];  // per query block, per 64-block chunk
+  __shared__ float qb[SPARSE ? QB * D : 1];
+  __shared__ float redf[QB * NW];
+  __shared__ int redi[QB * NW];
+  __shared__ int counts[QB];
   __shared__ int nunion_s;
 
   const int N = a.N, Nb = a.Nb;
-  const int npairs = (Nb + 1) >> 1;
-  const int G = a.BH * npairs;
+  const int ngroups = (Nb + QB - 1) / QB;
+  const int G = a.BH * ngroups;
   const int tile = xcd_remap((int)blockIdx.x, G);
-  const int bh = tile / npairs;
-  const int pair = tile - bh * npairs;
+  const int bh = tile / ngroups;
+  const int grp = tile - bh * ngroups;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int qsel = wave >> 1, qhalf = wave & 1;
   const int h = lane >> 5, l32 = lane & 31;
-  const int I = 2 * pair + qsel;
+  const int I = QB * grp + qsel;
   const bool qvalid = I < Nb;
-  const bool two = 2 * pair + 1 < Nb;
-  const int ntail = N - (Nb - 1) * kBlock;  // tokens in the last block
+  const int nrows = min(QB, Nb - QB * grp);   // valid query blocks of this group
+  const int ntail = N - (Nb - 1) * kBlock;    // tokens in the last block
+  const int nchunks = (Nb + 63) >> 6;          // 64-block chunks of virtual keys
 
   // ---------------------------------------------------------------- 1. route
   int nvirt = 0, nunion = Nb;
   if constexpr (SPARSE) {
-    if (tid < 2 * D) {
-      const int r = tid / D, d = tid % D;
-      const int Ir = 2 * pair + r;
-      qb[tid] = (Ir < Nb) ? a.qbar[((size_t)bh * Nb + Ir) * D + d] : 0.f;
+    for (int t = tid; t < QB * D; t += NT) {
+      const int r = t / D, d = t % D;
+      qb[t] = (r < nrows) ? a.qbar[((size_t)bh * Nb + QB * grp + r) * D + d] : 0.f;
     }
     __syncthreads();
     float* p = reinterpret_cast<float*>(smem);
-    proxy_row_pair<D, kThreads>(qb, a.kbar + (size_t)bh * Nb * D, Nb, a.scale, two, p);
+    proxy_rows<D, NT, QB>(qb, a.kbar + (size_t)bh * Nb * D, Nb, a.scale, nrows, p);
     __syncthreads();
-    threshold_rows<kThreads>(p, Nb, two, a.tau, flags, redf, redi, counts);
-    build_union<kThreads>(flags, Nb, ulist, &nunion_s, redi);
+    threshold_rows<NT, QB>(p, Nb, nrows, a.tau, flags, redf, redi, counts);
+    build_union<NT>(flags, Nb, ulist, &nunion_s, redi);
     nunion = nunion_s;
-    if (a.kept && tid == 0) {
-      a.kept[(size_t)bh * Nb + 2 * pair] = counts[0];
-      if (two) a.kept[(size_t)bh * Nb + 2 * pair + 1] = counts[1];
+    if (a.kept && tid < nrows) a.kept[(size_t)bh * Nb + QB * grp + tid] = counts[tid];
+    if (a.correction) {
+      nvirt = nchunks;
+      // skipbits[r][c] bit j: block 64c + j exists and query block r skips it
+      for (int rc = wave; rc < QB * nchunks; rc += NW) {
+        const int r = rc / nchunks, c = rc - r * nchunks;
+        const int J = 64 * c + lane;
+        const bool skip = J < Nb && !((flags[J < Nb ? J : 0] >> r) & 1);
+        const uint64_t bits = __ballot(skip);
+        if (lane == 0) skipbits[r * (kMaxNb / 64) + c] = bits;
+      }
+      __syncthreads();
     }
-    if (a.correction) nvirt = a.Nbp / 64;
   }
   const int ntiles = nvirt + nunion;
 
@@ -184,21 +246,23 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnArgs a) {
   }
   float qscale = 1.f;
   if constexpr (FP8) qscale = qvalid ? a.q_scale[(size_t)bh * Nb + I] : 0.f;
+  // Retire every global load issued so far, so that the only vector-memory
+  // operations in flight inside the main loop are the tile copies it counts.
+  wait_vmcnt<0>();
 
   // ------------------------------------------------------------ LDS staging
-  auto Kbuf = [&](int buf) -> uint8_t* { return smem + buf * C::KTILE; };
-  auto Vbuf = [&](int buf) -> uint8_t* { return smem + 2 * C::KTILE + buf * C::VTILE; };
+  const uint32_t smem_base = (uint32_t)(uintptr_t)smem;
   auto tile_block = [&](int it) -> int {
     if constexpr (SPARSE) return ulist[it - nvirt] & 0xFFF;
     return it;
   };
 
-  // Issue the global->LDS copies of tile `it` into buffer `buf`.  Wave w's
-  // i-th copy fills LDS bytes [(w + 4i) KiB, +1 KiB); lane l writes 16 bytes
-  // at +16*l, i.e. physical chunk pc of row r, which holds logical chunk
-  // pc ^ swz(r).  Rows past the end of the sequence re-read the last valid
-  // row (finite data; those keys are masked).
-  auto issue_tile = [&](int it, int buf) {
+  // Issue the LDS-DMA copies of tile `it` into stage `stg`.  Wave w's i-th
+  // copy fills LDS bytes [(w + NW*i) KiB, +1 KiB) of the K or V^T buffer; lane
+  // l writes 16 bytes at +16*l, i.e. physical chunk pc of row r, which holds
+  // logical chunk pc ^ swz(r).  Rows past the end of the sequence re-read the
+  // last valid row (finite data; those keys are masked).
+  auto issue_tile = [&](int it, int stg) {
     const uint8_t* ksrc;
     const uint8_t* vsrc;
     int kvalid = 64;
@@ -213,30 +277,30 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnArgs a) {
       vsrc = reinterpret_cast<const uint8_t*>(a.vt16 + ((size_t)bh * Nb + J) * D * kBlock);
       kvalid = min(kBlock, N - J * kBlock);
     }
-    uint8_t* kb = Kbuf(buf);
+    const uint32_t kb = smem_base + stg * C::STAGE;
+    const uint32_t vb = kb + C::KTILE;
     if (k8) {
 #pragma unroll
-      for (int i = 0; i < C::KTILE / 2 / 4096; ++i) {
-        const int P = (wave + 4 * i) * 1024 + 16 * lane;
+      for (int i = 0; i < KI8; ++i) {
+        const int P = (wave + NW * i) * 1024 + 16 * lane;
         const int row = P / C::KROW8, pc = (P % C::KROW8) / 16;
         const int src_row = min(row, kvalid - 1);
-        g2lds16(ksrc + src_row * C::KROW8 + swz_any<C::CPR8>(row, pc) * 16, kb + (wave + 4 * i) * 1024);
+        dma16(ksrc + src_row * C::KROW8 + swz_any<C::CPR8>(row, pc) * 16, kb + (wave + NW * i) * 1024);
       }
     } else {
 #pragma unroll
-      for (int i = 0; i < C::KTILE / 4096; ++i) {
-        const int P = (wave + 4 * i) * 1024 + 16 * lane;
+      for (int i = 0; i < KI16; ++i) {
+        const int P = (wave + NW * i) * 1024 + 16 * lane;
         const int row = P / C::KROW16, pc = (P % C::KROW16) / 16;
         const int src_row = min(row, kvalid - 1);
-        g2lds16(ksrc + src_row * C::KROW16 + swz<C::CPR16>(row, pc) * 16, kb + (wave + 4 * i) * 1024);
+        dma16(ksrc + src_row * C::KROW16 + swz<C::CPR16>(row, pc) * 16, kb + (wave + NW * i) * 1024);
       }
     }
-    uint8_t* vb = Vbuf(buf);
 #pragma unroll
-    for (int i = 0; i < C::VTILE / 4096; ++i) {
-      const int P = (wave + 4 * i) * 1024 + 16 * lane;
+    for (int i = 0; i < VI; ++i) {
+      const int P = (wave + NW * i) * 1024 + 16 * lane;
       const int row = P / 128, pc = (P % 128) / 16;
-      g2lds16(vsrc + row * 128 + swz<8>(row, pc) * 16, vb + (wave + 4 * i) * 1024);
+      dma16(vsrc + row * 128 + swz<8>(row, pc) * 16, vb + (wave + NW * i) * 1024);
     }
   };
 
@@ -252,24 +316,27 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnArgs a) {
   const float log2_tail = log2f((float)ntail);
 
   // -------------------------------------------------------------- main loop
-  if (ntiles > 0) issue_tile(0, 0);
+#pragma unroll
+  for (int s = 0; s < ST - 1; ++s)
+    if (s < ntiles) issue_tile(s, s);
   for (int it = 0; it < ntiles; ++it) {
-    const int buf = it & 1;
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    const int stg = it % ST;
+    wait_tiles_ahead<LPT, ST - 2>(min(ST - 2, ntiles - 1 - it));
     __syncthreads();
-    if (it + 1 < ntiles) issue_tile(it + 1, buf ^ 1);
+    if (it + ST - 1 < ntiles) issue_tile(it + ST - 1, (it + ST - 1) % ST);
 
     const bool virt = it < nvirt;
     int J = 0;
     bool active = qvalid;
     if (!virt) {
-      J = tile_block(it);
+      J = __builtin_amdgcn_readfirstlane(tile_block(it));
       if constexpr (SPARSE) active = active && ((ulist[it - nvirt] >> (12 + qsel)) & 1);
     }
     if (!active) continue;
 
     // ---- S^T = K Q^T for the 64 keys of the tile (two 32-key MFMA tiles)
-    const uint8_t* Kb = Kbuf(buf);
+    const uint8_t* Kb = smem + stg * C::STAGE;
+    const uint8_t* Vb = Kb + C::KTILE;
     f32x16 s[2];
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
@@ -280,7 +347,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnArgs a) {
     if constexpr (FP8) {
       if (!virt) {
         k8 = true;
-        c2 *= a.k_scale[(size_t)bh * Nb + J];
+        c2 *= scalar_load_f32(a.k_scale + ((size_t)bh * Nb + J));
       }
     }
     if (k8) {
@@ -297,15 +364,25 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnArgs a) {
         }
       }
     } else {
+      bf16x8 ka[2][2];
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) {
+        const int krow = 32 * kt + kperm(l32);
+        ka[0][kt] = *reinterpret_cast<const bf16x8*>(Kb + krow * C::KROW16 + swz<C::CPR16>(krow, h) * 16);
+      }
 #pragma unroll
       for (int ks = 0; ks < C::KS; ++ks) {
+        if (ks + 1 < C::KS) {
 #pragma unroll
-        for (int kt = 0; kt < 2; ++kt) {
-          const int krow = 32 * kt + kperm(l32);
-          const bf16x8 ka = *reinterpret_cast<const bf16x8*>(
-              Kb + krow * C::KROW16 + swz<C::CPR16>(krow, 2 * ks + h) * 16);
-          s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qr[ks], s[kt], 0, 0, 0);
+          for (int kt = 0; kt < 2; ++kt) {
+            const int krow = 32 * kt + kperm(l32);
+            ka[(ks + 1) & 1][kt] = *reinterpret_cast<const bf16x8*>(
+                Kb + krow * C::KROW16 + swz<C::CPR16>(krow, 2 * (ks + 1) + h) * 16);
+          }
         }
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+          s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[ks & 1][kt], qr[ks], s[kt], 0, 0, 0);
       }
     }
 
@@ -313,15 +390,21 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnArgs a) {
     float x[2][16];
     const bool tail = !virt && J == Nb - 1 && ntail < kBlock;
     if (virt) {
+      // 64 virtual keys J = 64*it + kk; lane half h holds kk in
+      // [32kt + 8h, +8) (r < 8) and [32kt + 16 + 8h, +8) (r >= 8)
+      const uint64_t bits = skipbits[qsel * (kMaxNb / 64) + it];
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
+      for (int kt = 0; kt < 2; ++kt) {
+        const uint32_t lo = (uint32_t)(bits >> (32 * kt + 8 * h)) & 0xFFu;
+        const uint32_t hi = (uint32_t)(bits >> (32 * kt + 16 + 8 * h)) & 0xFFu;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
+          const bool live = ((r < 8 ? lo : hi) >> (r & 7)) & 1u;
           const int Jv = 64 * it + 32 * kt + key_of(r, h);
-          const bool live = Jv < Nb && !((flags[Jv < Nb ? Jv : 0] >> qsel) & 1);
           const float w = (Jv == Nb - 1) ? log2_tail : 6.0f;  // log2(n_J): 64 except the tail
           x[kt][r] = live ? fmaf(s[kt][r], c2, w) : kNegInf;
         }
+      }
     } else if (tail) {
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt)
@@ -366,7 +449,6 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnArgs a) {
     l_run += rs;
 
     // ---- O^T += V^T P^T
-    const uint8_t* Vb = Vbuf(buf);
 #pragma unroll
     for (int dt = 0; dt < C::DT; ++dt) {
       const int vrow = 32 * dt + l32;
@@ -400,14 +482,25 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnArgs a) {
   }
 }
 
+#ifndef SA_QB
+#define SA_QB 4
+#endif
+#ifndef SA_STAGES
+#define SA_STAGES 2
+#endif
+
 template <int D, bool FP8>
 hipError_t launch_d(const AttnArgs& a, hipStream_t st) {
-  const int npairs = (a.Nb + 1) / 2;
-  const dim3 grid((unsigned)(a.BH * npairs));
+  // D = 64 tiles are half the size: two query blocks per workgroup keep at
+  // least one DMA copy per wave and two workgroups per CU
+  constexpr int QB = D == 64 ? 2 : SA_QB;
+  constexpr int STG = SA_STAGES;
+  const int ngroups = (a.Nb + QB - 1) / QB;
+  const dim3 grid((unsigned)(a.BH * ngroups));
   if (a.sparse)
-    hipLaunchKernelGGL((attn_kernel<D, true, FP8>), grid, dim3(kThreads), 0, st, a);
+    hipLaunchKernelGGL((attn_kernel<D, true, FP8, QB, STG>), grid, dim3(128 * QB), 0, st, a);
   else
-    hipLaunchKernelGGL((attn_kernel<D, false, FP8>), grid, dim3(kThreads), 0, st, a);
+    hipLaunchKernelGGL((attn_kernel<D, false, FP8, QB, STG>), grid, dim3(128 * QB), 0, st, a);
   return hipGetLastError();
 }
 

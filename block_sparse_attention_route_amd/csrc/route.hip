@@ -33,9 +33,9 @@ __global__ __launch_bounds__(256) void route_kernel(RouteArgs a) {
     qb[tid] = (I < a.Nb) ? a.qbar[((size_t)bh * a.Nb + I) * D + d] : 0.f;
   }
   __syncthreads();
-  proxy_row_pair<D, 256>(qb, a.kbar + (size_t)bh * a.Nb * D, a.Nb, a.scale, two, p);
+  proxy_rows<D, 256, 2>(qb, a.kbar + (size_t)bh * a.Nb * D, a.Nb, a.scale, two ? 2 : 1, p);
   __syncthreads();
-  threshold_rows<256>(p, a.Nb, two, a.tau, flags, redf, redi, counts);
+  threshold_rows<256, 2>(p, a.Nb, two ? 2 : 1, a.tau, flags, redf, redi, counts);
 
   uint8_t* m0 = a.mask + ((size_t)bh * a.Nb + I0) * a.Nb;
   for (int J = tid; J < a.Nb; J += 256) {

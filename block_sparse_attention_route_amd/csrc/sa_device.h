@@ -75,128 +75,143 @@ __device__ __forceinline__ int wave_sum_int(int x) {
 // Routing (Sol-Attn page, "Abstract": query-dependent threshold on a pooled
 // score, selected on chip without materialising a proxy map).
 //
-// proxy_row_pair() evaluates p_IJ = scale * (qbar_I . kbar_J) for one or two
-// query blocks against every key block J in float32, in one fixed order:
-// 16 lanes share a key row, lane j of the 16 accumulates dims
-// [j*D/16, (j+1)*D/16) with sequential fmaf, then a fixed xor-tree over the
-// 16 lanes.  The values therefore do not depend on how many waves run it, and
-// the standalone route kernel and the fused attention kernel, which both call
-// this routine, obtain identical bits.
+// proxy_rows() evaluates p_IJ = scale * (qbar_I . kbar_J) for QB query blocks
+// against every key block J in float32, in one fixed order: 16 lanes share a
+// key row, lane j of the 16 accumulates dims [j*D/16, (j+1)*D/16) with
+// sequential fmaf, then a fixed xor tree over the 16 lanes.  The value of a
+// pair (I, J) therefore does not depend on QB or on the number of threads, so
+// the standalone route kernel and every attention kernel, which all call this
+// routine, obtain identical bits.
 //
-// qbar: LDS, [2][D] (row 1 ignored when two == false).  kbar: global [Nb][D].
-// p: LDS, [2][Nb] output.  Returns nothing; p is complete after a barrier.
+// qbar: LDS [QB][D] (rows >= nrows ignored).  kbar: global [Nb][D].
+// p: LDS [QB][Nb] output, complete after a barrier.
 // ---------------------------------------------------------------------------
-template <int D, int NTHREADS>
-__device__ __forceinline__ void proxy_row_pair(const float* __restrict__ qbar,
-                                               const float* __restrict__ kbar, int Nb,
-                                               float scale, bool two, float* __restrict__ p) {
+template <int D, int NTHREADS, int QB>
+__device__ __forceinline__ void proxy_rows(const float* __restrict__ qbar,
+                                           const float* __restrict__ kbar, int Nb, float scale,
+                                           int nrows, float* __restrict__ p) {
   constexpr int DPL = D / 16;  // dims per lane
   const int tid = threadIdx.x;
   const int sub = tid & 15;
   const int slot = tid >> 4;
   constexpr int ROWS_PER_PASS = NTHREADS / 16;
-  float q0[DPL], q1[DPL];
+  float qv[QB][DPL];
 #pragma unroll
-  for (int e = 0; e < DPL; ++e) {
-    q0[e] = qbar[sub * DPL + e];
-    q1[e] = two ? qbar[D + sub * DPL + e] : 0.f;
-  }
+  for (int r = 0; r < QB; ++r)
+#pragma unroll
+    for (int e = 0; e < DPL; ++e) qv[r][e] = (r < nrows) ? qbar[r * D + sub * DPL + e] : 0.f;
   for (int J0 = 0; J0 < Nb; J0 += ROWS_PER_PASS) {
     const int J = J0 + slot;
-    float a0 = 0.f, a1 = 0.f;
+    float acc[QB];
+#pragma unroll
+    for (int r = 0; r < QB; ++r) acc[r] = 0.f;
     if (J < Nb) {
       const f32x4* row = reinterpret_cast<const f32x4*>(kbar + (size_t)J * D + sub * DPL);
 #pragma unroll
       for (int e4 = 0; e4 < DPL / 4; ++e4) {
-        f32x4 kv = row[e4];
+        const f32x4 kv = row[e4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          a0 = fmaf(q0[e4 * 4 + e], kv[e], a0);
-          a1 = fmaf(q1[e4 * 4 + e], kv[e], a1);
-        }
+        for (int e = 0; e < 4; ++e)
+#pragma unroll
+          for (int r = 0; r < QB; ++r) acc[r] = fmaf(qv[r][e4 * 4 + e], kv[e], acc[r]);
       }
     }
     // fixed xor tree over the 16 lanes that share row J
 #pragma unroll
-    for (int off = 1; off < 16; off <<= 1) {
-      a0 = a0 + __shfl_xor(a0, off);
-      a1 = a1 + __shfl_xor(a1, off);
-    }
+    for (int off = 1; off < 16; off <<= 1)
+#pragma unroll
+      for (int r = 0; r < QB; ++r) acc[r] = acc[r] + __shfl_xor(acc[r], off);
     if (J < Nb && sub == 0) {
-      p[J] = a0 * scale;
-      if (two) p[Nb + J] = a1 * scale;
+#pragma unroll
+      for (int r = 0; r < QB; ++r)
+        if (r < nrows) p[r * Nb + J] = acc[r] * scale;
     }
   }
 }
 
-// Row maxima of p (one or two rows) and the keep flags
-// flags[J] = (p[0][J] >= m0 - tau) | (p[1][J] >= m1 - tau) << 1, plus the
-// kept count of each row.  red: LDS scratch of >= 2*NTHREADS/64 floats and
-// ints.  Requires a barrier between proxy_row_pair() and this call; ends
-// with the flags, counts[2] complete (after the final barrier inside).
-template <int NTHREADS>
-__device__ __forceinline__ void threshold_rows(const float* __restrict__ p, int Nb, bool two,
+// Row maxima of the first nrows rows of p and the keep flags
+// flags[J] = OR over rows r of [p[r][J] >= m_r - tau] << r, plus the kept
+// count of each row in counts[r].  redf, redi: LDS scratch of QB*NTHREADS/64
+// entries.  Needs a barrier between proxy_rows() and this call; ends with a
+// barrier after which flags and counts are complete.
+template <int NTHREADS, int QB>
+__device__ __forceinline__ void threshold_rows(const float* __restrict__ p, int Nb, int nrows,
                                                float tau, uint8_t* __restrict__ flags,
                                                float* __restrict__ redf, int* __restrict__ redi,
                                                int* __restrict__ counts) {
   constexpr int NW = NTHREADS / 64;
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
-  float m0 = kNegInf, m1 = kNegInf;
-  for (int J = tid; J < Nb; J += NTHREADS) {
-    m0 = fmaxf(m0, p[J]);
-    if (two) m1 = fmaxf(m1, p[Nb + J]);
-  }
-  m0 = wave_max(m0);
-  m1 = wave_max(m1);
-  if (lane == 0) {
-    redf[wave] = m0;
-    redf[NW + wave] = m1;
-  }
-  __syncthreads();
-  m0 = redf[0];
-  m1 = redf[NW];
+  float m[QB];
 #pragma unroll
-  for (int w = 1; w < NW; ++w) {
-    m0 = fmaxf(m0, redf[w]);
-    m1 = fmaxf(m1, redf[NW + w]);
-  }
-  const float thr0 = m0 - tau;
-  const float thr1 = m1 - tau;
-  int c0 = 0, c1 = 0;
-  for (int J = tid; J < Nb; J += NTHREADS) {
-    const int k0 = p[J] >= thr0 ? 1 : 0;
-    const int k1 = (two && p[Nb + J] >= thr1) ? 1 : 0;
-    flags[J] = (uint8_t)(k0 | (k1 << 1));
-    c0 += k0;
-    c1 += k1;
-  }
-  c0 = wave_sum_int(c0);
-  c1 = wave_sum_int(c1);
-  if (lane == 0) {
-    redi[wave] = c0;
-    redi[NW + wave] = c1;
+  for (int r = 0; r < QB; ++r) m[r] = kNegInf;
+  for (int J = tid; J < Nb; J += NTHREADS)
+#pragma unroll
+    for (int r = 0; r < QB; ++r)
+      if (r < nrows) m[r] = fmaxf(m[r], p[r * Nb + J]);
+#pragma unroll
+  for (int r = 0; r < QB; ++r) {
+    m[r] = wave_max(m[r]);
+    if (lane == 0) redf[r * NW + wave] = m[r];
   }
   __syncthreads();
-  if (tid == 0) {
-    int s0 = 0, s1 = 0;
-    for (int w = 0; w < NW; ++w) {
-      s0 += redi[w];
-      s1 += redi[NW + w];
+  float thr[QB];
+#pragma unroll
+  for (int r = 0; r < QB; ++r) {
+    float mm = redf[r * NW];
+#pragma unroll
+    for (int w = 1; w < NW; ++w) mm = fmaxf(mm, redf[r * NW + w]);
+    thr[r] = mm - tau;
+  }
+  int c[QB];
+#pragma unroll
+  for (int r = 0; r < QB; ++r) c[r] = 0;
+  for (int J = tid; J < Nb; J += NTHREADS) {
+    int f = 0;
+#pragma unroll
+    for (int r = 0; r < QB; ++r) {
+      const int k = (r < nrows && p[r * Nb + J] >= thr[r]) ? 1 : 0;
+      f |= k << r;
+      c[r] += k;
     }
-    counts[0] = s0;
-    counts[1] = s1;
+    flags[J] = (uint8_t)f;
+  }
+#pragma unroll
+  for (int r = 0; r < QB; ++r) {
+    c[r] = wave_sum_int(c[r]);
+    if (lane == 0) redi[r * NW + wave] = c[r];
+  }
+  __syncthreads();
+  if (tid < QB) {
+    int sum = 0;
+    for (int w = 0; w < NW; ++w) sum += redi[tid * NW + w];
+    counts[tid] = sum;
   }
   __syncthreads();
 }
 
-// XCD-aware tile order: workgroups are handed to the 8 XCDs round-robin, so
-// workgroup w runs on XCD w % 8.  Give each XCD one contiguous range of tiles
-// (adjacent query blocks of the same head share key blocks in that XCD's L2).
+#ifndef SA_XCD_CHUNK
+#define SA_XCD_CHUNK 64
+#endif
+
+// XCD-aware tile order.  Workgroups are handed to the 8 XCDs round-robin, so
+// workgroup w runs on XCD w % 8 as that XCD's (w / 8)-th workgroup.  Tiles
+// are cut into chunks of SA_XCD_CHUNK consecutive tiles (adjacent query
+// blocks of one head, about as many as an XCD holds at once) and chunk c goes
+// to XCD c % 8: the workgroups resident on one XCD share key blocks in its
+// L2, and all eight XCDs stay on the same head at a time, so the head's K/V
+// stays resident in the shared last-level cache.  SA_XCD_CHUNK = 0 keeps the
+// plain order.  Tiles past the last whole round keep their own index.
 __device__ __forceinline__ int xcd_remap(int w, int G) {
-  const int q = G >> 3, r = G & 7;
-  const int x = w & 7, i = w >> 3;
-  return x * q + (x < r ? x : r) + i;
+  constexpr int CH = SA_XCD_CHUNK;
+  if constexpr (CH == 0) {
+    return w;
+  } else {
+    const int full = G / (8 * CH) * (8 * CH);
+    if (w >= full) return w;
+    const int x = w & 7, i = w >> 3;
+    return (i / CH) * (8 * CH) + x * CH + (i % CH);
+  }
 }
 
 }  // namespace sa

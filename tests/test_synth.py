@@ -1,0 +1,88 @@
+"""The seeded input generator (CPU only): determinism, shapes, the logit-scale
+normalisation, sink tokens and the per-block fp8 quantisation."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from block_sparse_attention_route_amd import synth
+
+
+def _small(dtype="bf16", **kw):
+    return synth.Workload("small", 1, 2, 3, 10, 13, 64, dtype, (2.0,), True, seed=5, **kw)
+
+
+def test_deterministic():
+    a = synth.generate(_small())
+    b = synth.generate(_small(), threads=1)
+    assert torch.equal(a.q, b.q) and torch.equal(a.k, b.k) and torch.equal(a.v, b.v)
+
+
+def test_heads_and_batches_differ():
+    wl = synth.Workload("cfg", 2, 2, 2, 8, 8, 64, "bf16", (4.0,), True, seed=4)
+    x = synth.generate(wl)
+    assert not torch.equal(x.q[0, 0], x.q[1, 0])   # cond / uncond streams differ
+    assert not torch.equal(x.q[0, 0], x.q[0, 1])
+
+
+@pytest.mark.parametrize("name", sorted(synth.WORKLOADS))
+def test_workload_shapes(name):
+    wl = synth.workload(name)
+    assert wl.N == wl.T * wl.Hg * wl.Wg
+    assert wl.Nb == math.ceil(wl.N / 64)
+    small = wl.with_(B=1, H=1, T=1)
+    x = synth.generate(small)
+    expect = {"f32": torch.float32, "bf16": torch.bfloat16, "fp8": torch.float8_e4m3fn}[wl.dtype]
+    assert x.q.dtype == expect and x.q.shape == (1, 1, small.N, wl.D)
+    assert x.v.dtype == (torch.float32 if wl.dtype == "f32" else torch.bfloat16)
+
+
+def test_known_shapes():
+    assert synth.workload("720p").N == 75600 and synth.workload("720p").Nb == 1182
+    assert synth.workload("480p").N == 32760 and synth.workload("480p").N % 64 == 56
+    assert synth.workload("1080p").N == 171360 and synth.workload("1080p").N % 64 == 32
+    assert synth.workload("tiny").N == 1024
+
+
+def test_logit_std_about_three():
+    wl = synth.Workload("std", 1, 1, 4, 16, 16, 64, "f32", (4.0,), True, seed=9)
+    x = synth.generate(wl)
+    q, k = x.q[0, 0].double(), x.k[0, 0].double()
+    s = (q @ k.T) / math.sqrt(64)
+    assert 2.5 < float(s.std()) < 3.5
+
+
+def test_sink_tokens_have_four_times_mean_norm():
+    wl = _small("f32", n_sink=2)
+    x = synth.generate(wl)
+    ref = synth.generate(_small("f32"))
+    for t, t0 in ((x.q[0, 0], ref.q[0, 0]), (x.k[0, 0], ref.k[0, 0])):
+        # rows 0 and 1 become 4x the mean row norm of the unmodified tensor
+        target = 4.0 * float(t0.double().norm(dim=1).mean())
+        norms = t.double().norm(dim=1)
+        assert abs(float(norms[0]) - target) < 1e-4 * target
+        assert abs(float(norms[1]) - target) < 1e-4 * target
+        assert torch.equal(t[2:], t0[2:])
+
+
+def test_fp8_quantisation():
+    wl = synth.Workload("f8", 1, 1, 2, 9, 9, 64, "fp8", (4.0,), True, seed=3)   # N = 162: ragged
+    x = synth.generate(wl)
+    codes = x.q[0, 0].to(torch.float32)
+    scale = x.q_scale[0, 0]
+    assert scale.shape == (wl.Nb,)
+    for J in range(wl.Nb):
+        blk = codes[64 * J: 64 * J + 64]
+        assert float(blk.abs().max()) <= 448.0
+        # the largest code of each block sits at (or one e4m3 step below) 448
+        assert float(blk.abs().max()) >= 416.0
+    q64, _, _ = x.head64(0, 0)
+    rep = np.repeat(scale.numpy().astype(np.float64), 64)[: wl.N]
+    np.testing.assert_array_equal(q64, codes.numpy().astype(np.float64) * rep[:, None])
+
+
+def test_fp8_zero_block_scale_is_one():
+    codes, scale = synth._fp8_quantise(torch.zeros(70, 8), 64)
+    assert torch.equal(scale, torch.ones(2))
+    assert float(codes.to(torch.float32).abs().max()) == 0.0
