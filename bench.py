@@ -124,6 +124,8 @@ def main() -> None:
     ap.add_argument("--dense-steps", type=int, default=2)
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="also run one 1 GiB device-to-device copy (reference for the PMC byte counters)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -193,11 +195,16 @@ def main() -> None:
     peak = PEAK_BF16_TFLOPS
     if wl.dtype == "fp8":
         peak = 1.0 / (0.5 / PEAK_FP8_TFLOPS + 0.5 / PEAK_BF16_TFLOPS)   # QK^T fp8, PV bf16
-    pool_bytes = (wl.B * wl.H * wl.N * wl.D * (3 if wl.dtype == "f32" else 2) * 4 if wl.dtype == "f32"
-                  else wl.B * wl.H * wl.N * wl.D * ((1 if wl.dtype == "fp8" else 2) * 2 + 2))
-    pool_bytes += wl.B * wl.H * wl.Nb * wl.D * 4 * 3   # fp32 means written
+    # pool: algorithmic bytes = Q, K, V read once (+ fp8 block scales), the three
+    # fp32 mean tensors, and for bf16 V the bf16 key/value means (padded to a
+    # multiple of 64 blocks) and V regrouped per 64-key block (padded to 64 rows)
+    bh, nbp = wl.B * wl.H, (wl.Nb + 63) // 64 * 64
+    e_qk = {"f32": 4, "bf16": 2, "fp8": 1}[wl.dtype]
+    e_v = 4 if wl.dtype == "f32" else 2
+    pool_bytes = bh * wl.N * wl.D * (2 * e_qk + e_v) + (2 * bh * wl.Nb * 4 if wl.dtype == "fp8" else 0)
+    pool_bytes += 3 * bh * wl.Nb * wl.D * 4
     if wl.dtype != "f32":
-        pool_bytes += wl.B * wl.H * wl.Nb * wl.D * 64 * 2   # regrouped V written
+        pool_bytes += 2 * bh * nbp * wl.D * 2 + bh * wl.Nb * wl.D * 64 * 2
     pool_avg = float(np.mean(pool_ms))
 
     traffic = None
@@ -226,6 +233,13 @@ def main() -> None:
         dense = {"ms": dms, "tflops": f_dense / (dms * 1e-3) / 1e12,
                  "frac_peak": f_dense / (dms * 1e-3) / 1e12 / peak, "sparse_speedup": dms / ms_step}
         del wsd, od, lsed
+
+    if args.calibrate_copy:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     cpu = None
     if not args.no_cpu_baseline:
