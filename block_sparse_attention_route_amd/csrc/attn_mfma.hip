@@ -6,10 +6,10 @@
 // blocks run in a single online-softmax pass, with blocks selected on chip and
 // no proxy map materialised.  Sol-Engine README (section "Sol-Attention"):
 // only the most relevant key blocks are computed, plus a light-weight
-// compensating operation.  Per workgroup (two adjacent 64-token query blocks
+// compensating operation.  Per workgroup (QB adjacent 64-token query blocks
 // of one head) this kernel:
 //
-//   1. route: evaluates the proxy rows p_IJ = s * qbar_I . kbar_J of both
+//   1. route: evaluates the proxy rows p_IJ = s * qbar_I . kbar_J of its
 //      query blocks into LDS (the shared float32 routine of sa_device.h),
 //      thresholds them at rowmax - tau and compacts the union of the kept
 //      key blocks into an index list in LDS -- nothing is written to HBM;
@@ -40,13 +40,31 @@
 // each XCD works on a chunk of adjacent query blocks while all XCDs stay on
 // the same head (shared key blocks hit in that XCD's L2, the head's K/V stays
 // in the last-level cache).
+//
+// Softmax.  The running maximum is raised lazily: only when a row's new
+// maximum exceeds the one in use by more than 2^8 are l and the accumulators
+// rescaled.  This is exact -- numerator and denominator carry the same stale
+// maximum, and P <= 2^8 stays well inside bf16 -- and makes the rescale rare.
+// Row sums are taken over the bf16-rounded P that enters the PV product.
+#include <type_traits>
+
 #include "sa_device.h"
 #include "sa_kernels.h"
 
 namespace sa {
 namespace {
 
-constexpr int kThreads = 256;
+constexpr float kLazy = 8.0f;  // log2 headroom of the lazily raised running maximum
+
+// Kinds of key tile: block means (correction), a full exact block, the
+// ragged last exact block.
+constexpr int kVirt = 0, kPlain = 1, kTail = 2;
+
+// max of x over lanes l and l^32 (v_permlane32_swap exchanges the halves)
+__device__ __forceinline__ float xor32_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
 
 // Key row that MFMA row m of a 32-key tile reads: swap bits 2 and 3.
 __device__ __forceinline__ int kperm(int m) { return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1); }
@@ -319,20 +337,24 @@ __global__ __launch_bounds__(128 * QB, QB == 2 ? 2 : 1) void attn_kernel(AttnArg
 #pragma unroll
   for (int s = 0; s < ST - 1; ++s)
     if (s < ntiles) issue_tile(s, s);
-  for (int it = 0; it < ntiles; ++it) {
+  // One tile: publish it, prefetch the tile ST-1 ahead, then S^T, softmax
+  // and PV.  KIND selects the masks at compile time, so the plain exact
+  // tiles -- nearly all of them -- carry no per-key selects.
+  auto step = [&](int it, auto kindc) __attribute__((always_inline)) {
+    constexpr int KIND = decltype(kindc)::value;
     const int stg = it % ST;
     wait_tiles_ahead<LPT, ST - 2>(min(ST - 2, ntiles - 1 - it));
     __syncthreads();
     if (it + ST - 1 < ntiles) issue_tile(it + ST - 1, (it + ST - 1) % ST);
 
-    const bool virt = it < nvirt;
+    constexpr bool virt = KIND == kVirt;
     int J = 0;
     bool active = qvalid;
     if (!virt) {
       J = __builtin_amdgcn_readfirstlane(tile_block(it));
       if constexpr (SPARSE) active = active && ((ulist[it - nvirt] >> (12 + qsel)) & 1);
     }
-    if (!active) continue;
+    if (!active) return;
 
     // ---- S^T = K Q^T for the 64 keys of the tile (two 32-key MFMA tiles)
     const uint8_t* Kb = smem + stg * C::STAGE;
@@ -386,65 +408,63 @@ __global__ __launch_bounds__(128 * QB, QB == 2 ? 2 : 1) void attn_kernel(AttnArg
       }
     }
 
-    // ---- scaled logits (log2 units) with the tile's mask / log-multiplicity
-    float x[2][16];
-    const bool tail = !virt && J == Nb - 1 && ntail < kBlock;
-    if (virt) {
-      // 64 virtual keys J = 64*it + kk; lane half h holds kk in
-      // [32kt + 8h, +8) (r < 8) and [32kt + 16 + 8h, +8) (r >= 8)
+    // ---- masks and log-multiplicities, applied to the raw scores (c2 > 0)
+    if constexpr (KIND == kVirt) {
+      // 64 virtual keys J = 64*it + 32kt + key_of(r, h): live iff this query
+      // block skips J; weight log2(n_J) = 6, or log2 of the tail's size
       const uint64_t bits = skipbits[qsel * (kMaxNb / 64) + it];
+      const float inv_c2 = 1.f / c2;
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt) {
-        const uint32_t lo = (uint32_t)(bits >> (32 * kt + 8 * h)) & 0xFFu;
-        const uint32_t hi = (uint32_t)(bits >> (32 * kt + 16 + 8 * h)) & 0xFFu;
+      for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const bool live = ((r < 8 ? lo : hi) >> (r & 7)) & 1u;
-          const int Jv = 64 * it + 32 * kt + key_of(r, h);
-          const float w = (Jv == Nb - 1) ? log2_tail : 6.0f;  // log2(n_J): 64 except the tail
-          x[kt][r] = live ? fmaf(s[kt][r], c2, w) : kNegInf;
+          const int kk = 32 * kt + key_of(r, h);
+          const bool live = (bits >> kk) & 1u;
+          const float w = (64 * it + kk == Nb - 1) ? log2_tail : 6.0f;
+          s[kt][r] = live ? fmaf(w, inv_c2, s[kt][r]) : kNegInf;
         }
-      }
-    } else if (tail) {
+    } else if constexpr (KIND == kTail) {
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
         for (int r = 0; r < 16; ++r)
-          x[kt][r] = (32 * kt + key_of(r, h) < ntail) ? s[kt][r] * c2 : kNegInf;
-    } else {
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) x[kt][r] = s[kt][r] * c2;
+          if (32 * kt + key_of(r, h) >= ntail) s[kt][r] = kNegInf;
     }
 
-    // ---- online softmax (row = this lane's query; keys split with lane^32)
-    float mt = kNegInf;
+    // ---- online softmax (row = this lane's query; keys split with lane^32).
+    // The maximum in use is raised only when a row's maximum exceeds it by
+    // more than 2^kLazy: exact, since numerator and denominator share it.
+    float mt = s[0][0];
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) mt = fmaxf(mt, x[kt][r]);
-    mt = fmaxf(mt, __shfl_xor(mt, 32));
-    const float mnew = fmaxf(m_run, mt);
-    const float muse = (mnew == kNegInf) ? 0.f : mnew;
-    if (__any(mnew > m_run)) {
-      const float alpha = __builtin_amdgcn_exp2f(m_run - muse);
+      for (int r = 0; r < 16; ++r) mt = fmaxf(mt, s[kt][r]);
+    mt = xor32_max(mt) * c2;
+    if (__builtin_expect(__any(mt > m_run + kLazy), 0)) {
+      const float mn = fmaxf(m_run, mt);
+      const float alpha = (mn == kNegInf) ? 1.f : __builtin_amdgcn_exp2f(m_run - mn);
+      m_run = mn;
       l_run *= alpha;
 #pragma unroll
       for (int dt = 0; dt < C::DT; ++dt)
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[dt][r] *= alpha;
     }
-    m_run = mnew;
+    const float negm = (m_run == kNegInf) ? 0.f : -m_run;
     bf16x8 pb[4];
     float rs = 0.f;
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    const bf16x2 ones = {static_cast<__bf16>(1.f), static_cast<__bf16>(1.f)};
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float pr = __builtin_amdgcn_exp2f(x[kt][r] - muse);
-        rs += pr;
-        pb[2 * kt + (r >> 3)][r & 7] = static_cast<__bf16>(pr);
+      for (int r = 0; r < 16; r += 2) {
+        const __bf16 b0 = static_cast<__bf16>(__builtin_amdgcn_exp2f(fmaf(s[kt][r], c2, negm)));
+        const __bf16 b1 = static_cast<__bf16>(__builtin_amdgcn_exp2f(fmaf(s[kt][r + 1], c2, negm)));
+        pb[2 * kt + (r >> 3)][r & 7] = b0;
+        pb[2 * kt + (r >> 3)][(r & 7) + 1] = b1;
+        const bf16x2 pair = {b0, b1};
+        rs = __builtin_amdgcn_fdot2_f32_bf16(pair, ones, rs, false);
       }
     l_run += rs;
 
@@ -458,7 +478,13 @@ __global__ __launch_bounds__(128 * QB, QB == 2 ? 2 : 1) void attn_kernel(AttnArg
         acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[k4], acc[dt], 0, 0, 0);
       }
     }
-  }
+    };
+  // virtual (correction) tiles first, then the exact tiles of the union list
+  // in key order, the ragged last key block -- always last -- on its own
+  const bool has_tail = ntiles > nvirt && ntail < kBlock && tile_block(ntiles - 1) == Nb - 1;
+  for (int it = 0; it < nvirt; ++it) step(it, std::integral_constant<int, kVirt>{});
+  for (int it = nvirt; it < ntiles - (has_tail ? 1 : 0); ++it) step(it, std::integral_constant<int, kPlain>{});
+  if (has_tail) step(ntiles - 1, std::integral_constant<int, kTail>{});
 
   // --------------------------------------------------------------- 4. epilogue
   const float lt = l_run + __shfl_xor(l_run, 32);
