@@ -12,4 +12,5 @@ from .attention import (  # noqa: F401
     forward_head,
     proxy_scores,
     route,
+    route_topk,
 )

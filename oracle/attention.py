@@ -33,15 +33,20 @@ The pages give no formula, so this module fixes the plainest concrete reading
   "score column" of block J;
 * the output is the softmax over the union of exact logits (kept blocks) and
   correction logits (skipped blocks, if correction is on), with natural-log
-  LSE lse_i = M_i + ln Z_i.
+  LSE lse_i = M_i + ln Z_i;
+* alternatively (route_topk) a fixed budget: each query block keeps the topk
+  key blocks of largest proxy, equal proxies in increasing block order --
+  the paper review of the Sol Video Inference Engine (xllm-io blog) runs
+  PISA at block size 64 and a fixed sparsity rather than a threshold.
 
 It is evaluated here as the two-pass definition above in float64, not as an
 online softmax: first every logit of a row, then its max, then the sums.
 Each function below says which step it is.
 
-Pinned by tests/test_oracle_pins.py (closed forms of hand-derived cases,
-pure-Python brute force, library special cases, invariants).  Parity
-unpinned: none.
+Pinned by tests/test_oracle_pins.py and tests/test_oracle_topk.py (closed
+forms of hand-derived cases, pure-Python brute force, library special cases,
+invariants); tests/test_oracle_mutants.py checks that planted mistakes fail
+those pins.  Parity unpinned: none.
 """
 from __future__ import annotations
 
@@ -55,6 +60,7 @@ __all__ = [
     "default_scale",
     "proxy_scores",
     "route",
+    "route_topk",
     "attend_rows",
     "forward_head",
     "forward",
@@ -126,6 +132,35 @@ def route(q: np.ndarray, k: np.ndarray, block: int, tau: float, scale: float | N
     return keep, p, m
 
 
+def route_topk(q: np.ndarray, k: np.ndarray, block: int, topk: int, scale: float | None = None):
+    """Fixed-budget routing: keep the min(topk, Nb) key blocks with the
+    largest proxy in each query block's row; equal proxies are taken in
+    increasing key-block order.
+
+    The paper review of the Sol Video Inference Engine (xllm-io blog,
+    technique list, item "Sparse Attention", and the LTX-2.3 pipeline
+    settings) runs PISA with block size 64 at a fixed sparsity of 0.9, i.e. a
+    per-query-block budget of key blocks rather than a threshold; the score
+    ranked is the same pooled proxy as in route().
+    Returns (keep bool [Nb, Nb], p [Nb, Nb], pk [Nb]) with pk[I] the proxy of
+    the last block kept in row I (the k-th largest).
+    """
+    topk = int(topk)
+    if topk < 1:
+        raise ValueError("topk must be >= 1")
+    p = proxy_scores(q, k, block, scale)
+    nb = p.shape[0]
+    kk = min(topk, nb)
+    keep = np.zeros((nb, nb), dtype=bool)
+    pk = np.empty(nb)
+    for I in range(nb):
+        # primary key: proxy, descending; secondary: block index, ascending
+        order = np.lexsort((np.arange(nb), -p[I]))
+        keep[I, order[:kk]] = True
+        pk[I] = p[I, order[kk - 1]]
+    return keep, p, pk
+
+
 def attend_rows(q_rows: np.ndarray, k: np.ndarray, v: np.ndarray, keep_row: np.ndarray,
                 block: int, correction: bool, scale: float | None = None):
     """Output and LSE of the rows of one query block, given its keep row.
@@ -168,18 +203,22 @@ def attend_rows(q_rows: np.ndarray, k: np.ndarray, v: np.ndarray, keep_row: np.n
 
 def forward_head(q, k, v, block: int = 64, tau: float = math.inf, correction: bool = True,
                  scale: float | None = None, keep: np.ndarray | None = None,
-                 qblocks=None):
+                 qblocks=None, topk: int | None = None):
     """Sparse attention of one (batch, head): returns (o [N, Dv], lse [N], keep).
 
     keep: optional externally supplied [Nb, Nb] mask replacing the routing
     (used to evaluate the definition on a mask that differs from this oracle's
     only inside the near-threshold band).  qblocks: optional iterable of query
-    block indices; rows of other blocks are left as NaN.
+    block indices; rows of other blocks are left as NaN.  topk: route with the
+    fixed budget of route_topk() instead of the threshold tau.
     """
     q = np.asarray(q, dtype=np.float64)
     N = q.shape[0]
     if keep is None:
-        keep, _, _ = route(q, k, block, tau, scale)
+        if topk:
+            keep, _, _ = route_topk(q, k, block, topk, scale)
+        else:
+            keep, _, _ = route(q, k, block, tau, scale)
     ranges = block_ranges(N, block)
     o = np.full((N, np.asarray(v).shape[1]), np.nan)
     lse = np.full(N, np.nan)
@@ -190,7 +229,7 @@ def forward_head(q, k, v, block: int = 64, tau: float = math.inf, correction: bo
 
 
 def forward(q, k, v, block: int = 64, tau: float = math.inf, correction: bool = True,
-            scale: float | None = None):
+            scale: float | None = None, topk: int | None = None):
     """[B, H, N, D] batched form of forward_head; every (b, h) routes independently."""
     q = np.asarray(q, dtype=np.float64)
     B, H, N, _ = q.shape
@@ -200,7 +239,7 @@ def forward(q, k, v, block: int = 64, tau: float = math.inf, correction: bool = 
     for b in range(B):
         for h in range(H):
             o[b, h], lse[b, h], keep[b, h] = forward_head(q[b, h], k[b, h], v[b, h], block, tau,
-                                                          correction, scale)
+                                                          correction, scale, topk=topk)
     return o, lse, keep
 
 

@@ -15,6 +15,7 @@ import numpy as np
 import pytest
 
 from tests import test_oracle_pins as pins
+from tests import test_oracle_topk as topk_pins
 
 SRC = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "oracle", "attention.py")
 
@@ -35,6 +36,11 @@ MUTANTS = {
     "correction_value_is_key_mean": (
         "vbar = np.stack([v[slice(*ranges[J])].mean(axis=0) for J in skipped])",
         "vbar = np.stack([v[slice(*ranges[J])][0] for J in skipped])"),
+    "topk_ties_to_larger_index": (
+        "order = np.lexsort((np.arange(nb), -p[I]))", "order = np.lexsort((-np.arange(nb), -p[I]))"),
+    "topk_smallest_proxies": (
+        "order = np.lexsort((np.arange(nb), -p[I]))", "order = np.lexsort((np.arange(nb), p[I]))"),
+    "topk_one_short": ("keep[I, order[:kk]] = True", "keep[I, order[:max(kk - 1, 1)]] = True"),
 }
 
 
@@ -57,11 +63,18 @@ def _pins_pass(mod) -> bool:
                     pins.test_brute_force_tiny(N, block, D, tau, corr)
         pins.test_block_constant_kv_is_exact(1.0, 200)
         pins.test_keep_all_equals_sdpa(True)
+        topk_pins.orc = mod
+        for case in topk_pins._cases():
+            topk_pins.test_topk_hand_cases_closed_form(case, True)
+        topk_pins.test_topk_brute_force_with_ties()
+        for topk in (1, 2, 3):
+            topk_pins.test_topk_brute_force_tiny(12, 4, 3, topk, True)
         return True
     except AssertionError:
         return False
     finally:
         pins.orc = saved
+        topk_pins.orc = saved
 
 
 def _source() -> str:

@@ -52,7 +52,7 @@ def test_hand_cases_closed_form(case, corr):
 # pure-Python brute force (no numpy), written from the definition
 # ----------------------------------------------------------------------------
 
-def _brute(q, k, v, block, tau, correction, scale):
+def _brute(q, k, v, block, tau, correction, scale, topk=None):
     N, D = len(q), len(q[0])
     s = scale if scale else 1.0 / math.sqrt(D)
     blocks = []
@@ -75,8 +75,14 @@ def _brute(q, k, v, block, tau, correction, scale):
     lse = [None] * N
     for I, (a, b) in enumerate(blocks):
         p = [s * dot(qbar[I], kbar[J]) for J in range(len(blocks))]
-        m = max(p)
-        keep = [pj >= m - tau for pj in p]
+        if topk:
+            # the topk largest proxies; equal proxies in increasing block order
+            ranked = sorted(range(len(blocks)), key=lambda J: (-p[J], J))
+            chosen = set(ranked[:topk])
+            keep = [J in chosen for J in range(len(blocks))]
+        else:
+            m = max(p)
+            keep = [pj >= m - tau for pj in p]
         for i in range(a, b):
             terms = []  # (logit, multiplicity, value row)
             for J, (c0, c1) in enumerate(blocks):
