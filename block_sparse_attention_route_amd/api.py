@@ -51,7 +51,8 @@ class Shape(ctypes.Structure):
 
 class Params(ctypes.Structure):
     _fields_ = [("block", ctypes.c_int32), ("tau", ctypes.c_float),
-                ("correction", ctypes.c_int32), ("scale", ctypes.c_float)]
+                ("correction", ctypes.c_int32), ("scale", ctypes.c_float),
+                ("topk", ctypes.c_int32)]
 
 
 class Inputs(ctypes.Structure):
@@ -129,8 +130,16 @@ def make_shape(q: torch.Tensor, grid) -> Shape:
     return Shape(B, H, N, D, T, Hg, Wg)
 
 
-def make_params(tau: float, correction: bool = True, scale: float = 0.0) -> Params:
-    return Params(BLOCK, float(tau), int(bool(correction)), float(scale))
+def make_params(tau: float, correction: bool = True, scale: float = 0.0, topk: int = 0) -> Params:
+    return Params(BLOCK, float(tau), int(bool(correction)), float(scale), int(topk))
+
+
+def budget_blocks(sparsity: float, N: int) -> int:
+    """Key blocks kept per query block at a fixed sparsity (fraction of the
+    Nb key blocks skipped): ceil((1 - sparsity) * Nb), at least 1."""
+    if not 0.0 <= sparsity < 1.0:
+        raise ValueError("sparsity must be in [0, 1)")
+    return max(1, math.ceil((1.0 - sparsity) * _nb(N) - 1e-9))
 
 
 def make_inputs(q, k, v, q_scale=None, k_scale=None) -> Inputs:
@@ -173,17 +182,17 @@ def _workspace(nbytes: int, like: torch.Tensor, ws: torch.Tensor | None) -> torc
 
 
 def sa_pool(q, k, v, grid, *, tau: float = math.inf, correction: bool = True, scale: float = 0.0,
-            workspace: torch.Tensor | None = None, q_scale=None, k_scale=None) -> torch.Tensor:
+            workspace: torch.Tensor | None = None, q_scale=None, k_scale=None, topk: int = 0) -> torch.Tensor:
     """Step pool: block means (and V regrouped per 64-key block) into the workspace."""
     lib = load_library()
     ws = _workspace(sa_workspace_bytes(q, k, v, grid, q_scale, k_scale), q, workspace)
-    sh, pr, inp = make_shape(q, grid), make_params(tau, correction, scale), make_inputs(q, k, v, q_scale, k_scale)
+    sh, pr, inp = make_shape(q, grid), make_params(tau, correction, scale, topk), make_inputs(q, k, v, q_scale, k_scale)
     _check(lib.sa_pool(ctypes.byref(sh), ctypes.byref(pr), ctypes.byref(inp), _ptr(ws), ws.numel(), _stream(q)))
     return ws
 
 
-def sa_route(q, k, v, grid, *, tau: float, scale: float = 0.0, workspace=None, q_scale=None,
-             k_scale=None, mask=None, kept=None):
+def sa_route(q, k, v, grid, *, tau: float = math.inf, scale: float = 0.0, workspace=None, q_scale=None,
+             k_scale=None, mask=None, kept=None, topk: int = 0):
     """Steps pool + route: returns (mask uint8 [B,H,Nb,Nb], kept int32 [B,H,Nb])."""
     lib = load_library()
     B, H, N, _ = q.shape
@@ -193,7 +202,7 @@ def sa_route(q, k, v, grid, *, tau: float, scale: float = 0.0, workspace=None, q
         mask = torch.empty((B, H, Nb, Nb), dtype=torch.uint8, device=q.device)
     if kept is None:
         kept = torch.empty((B, H, Nb), dtype=torch.int32, device=q.device)
-    sh, pr, inp = make_shape(q, grid), make_params(tau, True, scale), make_inputs(q, k, v, q_scale, k_scale)
+    sh, pr, inp = make_shape(q, grid), make_params(tau, True, scale, topk), make_inputs(q, k, v, q_scale, k_scale)
     _check(lib.sa_route(ctypes.byref(sh), ctypes.byref(pr), ctypes.byref(inp), _ptr(mask), _ptr(kept),
                         _ptr(ws), ws.numel(), _stream(q)))
     return mask, kept
@@ -210,26 +219,26 @@ def _outs(q, v, out, lse, want_kept, kept):
     return out, lse, kept
 
 
-def sa_forward(q, k, v, grid, *, tau: float, correction: bool = True, scale: float = 0.0,
+def sa_forward(q, k, v, grid, *, tau: float = math.inf, correction: bool = True, scale: float = 0.0,
                workspace=None, q_scale=None, k_scale=None, out=None, lse=None, want_kept=False,
-               kept=None):
+               kept=None, topk: int = 0):
     """Pool + fused routed sparse attention with correction: returns (o, lse, kept or None)."""
     lib = load_library()
     ws = _workspace(sa_workspace_bytes(q, k, v, grid, q_scale, k_scale), q, workspace)
     out, lse, kept = _outs(q, v, out, lse, want_kept, kept)
-    sh, pr, inp = make_shape(q, grid), make_params(tau, correction, scale), make_inputs(q, k, v, q_scale, k_scale)
+    sh, pr, inp = make_shape(q, grid), make_params(tau, correction, scale, topk), make_inputs(q, k, v, q_scale, k_scale)
     _check(lib.sa_forward(ctypes.byref(sh), ctypes.byref(pr), ctypes.byref(inp), _ptr(out), _ptr(lse),
                           _ptr(kept), _ptr(ws), ws.numel(), _stream(q)))
     return out, lse, kept
 
 
-def sa_forward_pooled(q, k, v, grid, *, tau: float, correction: bool = True, scale: float = 0.0,
+def sa_forward_pooled(q, k, v, grid, *, tau: float = math.inf, correction: bool = True, scale: float = 0.0,
                       workspace, q_scale=None, k_scale=None, out=None, lse=None, want_kept=False,
-                      kept=None):
+                      kept=None, topk: int = 0):
     """The fused kernel alone; `workspace` must hold sa_pool's output for these inputs."""
     lib = load_library()
     out, lse, kept = _outs(q, v, out, lse, want_kept, kept)
-    sh, pr, inp = make_shape(q, grid), make_params(tau, correction, scale), make_inputs(q, k, v, q_scale, k_scale)
+    sh, pr, inp = make_shape(q, grid), make_params(tau, correction, scale, topk), make_inputs(q, k, v, q_scale, k_scale)
     _check(lib.sa_forward_pooled(ctypes.byref(sh), ctypes.byref(pr), ctypes.byref(inp), _ptr(out), _ptr(lse),
                                  _ptr(kept), _ptr(workspace), workspace.numel(), _stream(q)))
     return out, lse, kept

@@ -40,6 +40,7 @@ struct Req {
   int qk, v;
   bool empty;
   float scale, tau;
+  int topk;
   int correction;
   sa::WsLayout ws;
 };
@@ -89,10 +90,13 @@ sa_status check_shape_inputs(const sa_shape* sh, const sa_inputs* in, Req* r, bo
 sa_status check_params(const sa_params* p, Req* r) {
   if (!p) return fail(SA_ERR_NULL, "params is NULL");
   if (p->block != SA_BLOCK) return fail(SA_ERR_PARAM, "block must be %d (got %d)", SA_BLOCK, p->block);
-  if (std::isnan(p->tau) || p->tau < 0.f) return fail(SA_ERR_PARAM, "tau must be >= 0 or +inf");
+  if (p->topk < 0) return fail(SA_ERR_PARAM, "topk must be >= 0 (got %d)", p->topk);
+  if (p->topk == 0 && (std::isnan(p->tau) || p->tau < 0.f))
+    return fail(SA_ERR_PARAM, "tau must be >= 0 or +inf");
   if (p->correction != 0 && p->correction != 1) return fail(SA_ERR_PARAM, "correction must be 0 or 1");
   if (!std::isfinite(p->scale)) return fail(SA_ERR_PARAM, "scale must be finite");
   r->tau = p->tau;
+  r->topk = p->topk;
   r->correction = p->correction;
   r->scale = p->scale > 0.f ? p->scale : 1.0f / std::sqrt((float)r->D);
   return SA_OK;
@@ -178,6 +182,7 @@ sa::AttnArgs attn_args(const Req& r, const sa_inputs* in, void* o, float* lse, i
   a.v_elt = r.v;
   a.scale = r.scale;
   a.tau = r.tau;
+  a.topk = r.topk;
   a.correction = r.correction;
   a.sparse = sparse;
   return a;
@@ -264,6 +269,7 @@ SA_API sa_status sa_route(const sa_shape* shape, const sa_params* params, const 
   a.D = r.D;
   a.scale = r.scale;
   a.tau = r.tau;
+  a.topk = r.topk;
   a.mask = mask;
   a.kept = kept;
   return hip_status(sa::launch_route(a, st), "route kernel launch");
@@ -306,6 +312,7 @@ SA_API sa_status sa_dense_forward(const sa_shape* shape, float scale, const sa_i
   if (!std::isfinite(scale)) return fail(SA_ERR_PARAM, "scale must be finite");
   r.scale = scale > 0.f ? scale : 1.0f / std::sqrt((float)r.D);
   r.tau = INFINITY;
+  r.topk = 0;
   r.correction = 0;
   if (r.empty) return ok();
   if ((s = check_out(o, lse, nullptr)) != SA_OK) return s;

@@ -34,13 +34,18 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(AttnArgs a) {
   __shared__ float redf[8];
   __shared__ int redi[8];
   __shared__ int counts[2];
+  __shared__ int hist[SPARSE ? 256 : 1];
+  __shared__ uint32_t sel[SPARSE ? 3 : 1];
 
   if constexpr (SPARSE) {
     for (int d = lane; d < D; d += 64) qb[d] = a.qbar[((size_t)bh * Nb + I) * D + d];
     __syncthreads();
     proxy_rows<D, 64, 1>(qb, a.kbar + (size_t)bh * Nb * D, Nb, a.scale, 1, p);
     __syncthreads();
-    threshold_rows<64, 1>(p, Nb, 1, a.tau, flags, redf, redi, counts);
+    if (a.topk > 0)
+      topk_rows<64, 1>(p, Nb, 1, a.topk, flags, hist, sel, redi, counts);
+    else
+      threshold_rows<64, 1>(p, Nb, 1, a.tau, flags, redf, redi, counts);
     if (a.kept && lane == 0) a.kept[(size_t)bh * Nb + I] = counts[0];
   }
 

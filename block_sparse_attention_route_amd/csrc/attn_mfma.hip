@@ -11,8 +11,9 @@
 //
 //   1. route: evaluates the proxy rows p_IJ = s * qbar_I . kbar_J of its
 //      query blocks into LDS (the shared float32 routine of sa_device.h),
-//      thresholds them at rowmax - tau and compacts the union of the kept
-//      key blocks into an index list in LDS -- nothing is written to HBM;
+//      thresholds them at rowmax - tau (or keeps each row's topk largest,
+//      the fixed-budget mode) and compacts the union of the kept key blocks
+//      into an index list in LDS -- nothing is written to HBM;
 //   2. correct: streams the block means as "virtual keys": virtual key J has
 //      key kbar_J, value vbar_J and log-multiplicity log(n_J), and is masked
 //      for a query block that keeps J.  Its logit s * q_i . kbar_J is entry
@@ -192,6 +193,8 @@ __global__ __launch_bounds__(128 * QB, QB == 2 ? 2 : 1) void attn_kernel(AttnArg
   __shared__ float redf[QB * NW];
   __shared__ int redi[QB * NW];
   __shared__ int counts[QB];
+  __shared__ int hist[SPARSE ? QB * 256 : 1];
+  __shared__ uint32_t sel[SPARSE ? 3 * QB : 1];
   __shared__ int nunion_s;
 
   const int N = a.N, Nb = a.Nb;
@@ -220,7 +223,10 @@ __global__ __launch_bounds__(128 * QB, QB == 2 ? 2 : 1) void attn_kernel(AttnArg
     float* p = reinterpret_cast<float*>(smem);
     proxy_rows<D, NT, QB>(qb, a.kbar + (size_t)bh * Nb * D, Nb, a.scale, nrows, p);
     __syncthreads();
-    threshold_rows<NT, QB>(p, Nb, nrows, a.tau, flags, redf, redi, counts);
+    if (a.topk > 0)
+      topk_rows<NT, QB>(p, Nb, nrows, a.topk, flags, hist, sel, redi, counts);
+    else
+      threshold_rows<NT, QB>(p, Nb, nrows, a.tau, flags, redf, redi, counts);
     build_union<NT>(flags, Nb, ulist, &nunion_s, redi);
     nunion = nunion_s;
     if (a.kept && tid < nrows) a.kept[(size_t)bh * Nb + QB * grp + tid] = counts[tid];

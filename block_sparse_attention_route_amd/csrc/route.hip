@@ -2,7 +2,9 @@
 // routine on chip and never writes a mask): for each query block I of each
 // head, p_IJ = s * qbar_I . kbar_J over all key blocks J, its row maximum,
 // and the 0/1 keep mask p_IJ >= max_J p_IJ - tau (Sol-Attn project page,
-// section "Abstract": query-dependent threshold routing on a pooled score).
+// section "Abstract": query-dependent threshold routing on a pooled score),
+// or, with a fixed budget topk > 0, the topk largest p_IJ of the row (PISA's
+// fixed sparsity in the paper review of the Sol Video Inference Engine).
 //
 // One workgroup routes two adjacent query blocks of one head, exactly as the
 // fused kernel does, so that both obtain the same float32 bits.
@@ -25,6 +27,8 @@ __global__ __launch_bounds__(256) void route_kernel(RouteArgs a) {
   __shared__ float redf[8];
   __shared__ int redi[8];
   __shared__ int counts[2];
+  __shared__ int hist[2 * 256];
+  __shared__ uint32_t sel[6];
 
   const int tid = threadIdx.x;
   if (tid < 2 * D) {
@@ -35,7 +39,10 @@ __global__ __launch_bounds__(256) void route_kernel(RouteArgs a) {
   __syncthreads();
   proxy_rows<D, 256, 2>(qb, a.kbar + (size_t)bh * a.Nb * D, a.Nb, a.scale, two ? 2 : 1, p);
   __syncthreads();
-  threshold_rows<256, 2>(p, a.Nb, two ? 2 : 1, a.tau, flags, redf, redi, counts);
+  if (a.topk > 0)
+    topk_rows<256, 2>(p, a.Nb, two ? 2 : 1, a.topk, flags, hist, sel, redi, counts);
+  else
+    threshold_rows<256, 2>(p, a.Nb, two ? 2 : 1, a.tau, flags, redf, redi, counts);
 
   uint8_t* m0 = a.mask + ((size_t)bh * a.Nb + I0) * a.Nb;
   for (int J = tid; J < a.Nb; J += 256) {

@@ -190,6 +190,153 @@ __device__ __forceinline__ void threshold_rows(const float* __restrict__ p, int 
   __syncthreads();
 }
 
+// ---------------------------------------------------------------------------
+// Fixed-budget routing (the paper review of the Sol Video Inference Engine,
+// xllm-io blog, runs PISA at block size 64 and a fixed sparsity): row r keeps
+// the min(topk, Nb) key blocks of largest p[r][.], equal values in increasing
+// J.  The kept set is a function of the float32 values alone, so every caller
+// obtains the same set.  It is found by a radix select over order-preserving
+// 32-bit keys, most significant byte first (4 histogram passes), which
+// yields the k-th largest key T and how many blocks equal to T are kept; a
+// tie at T that is only partly kept is resolved by the rank among equal keys.
+//
+// p: LDS [QB][Nb] after a barrier.  hist: LDS [QB][256] ints.  sel: LDS
+// [3*QB] uint32 (key prefix, remaining count, count equal to T).  wsum: LDS
+// [QB * NTHREADS/64] ints.  Writes flags[J] (bit r) and counts[r]; ends with
+// a barrier.  Needs NTHREADS/64 >= QB.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t order_key(float f) {
+  const uint32_t u = __float_as_uint(f + 0.0f);  // -0 -> +0: equal values, equal keys
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+template <int NTHREADS, int QB>
+__device__ __forceinline__ void topk_rows(const float* __restrict__ p, int Nb, int nrows, int topk,
+                                          uint8_t* __restrict__ flags, int* __restrict__ hist,
+                                          uint32_t* __restrict__ sel, int* __restrict__ wsum,
+                                          int* __restrict__ counts) {
+  constexpr int NW = NTHREADS / 64;
+  static_assert(NW >= QB, "one wave per row for the digit search");
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int kk = min(topk, Nb);
+  uint32_t* prefix = sel;            // [QB] key bits fixed so far
+  uint32_t* need = sel + QB;         // [QB] blocks still to take among those matching prefix
+  uint32_t* neq = sel + 2 * QB;      // [QB] blocks whose key equals T
+  if (tid < QB) {
+    prefix[tid] = 0u;
+    need[tid] = (uint32_t)kk;
+    neq[tid] = 0u;
+  }
+#pragma unroll 1
+  for (int pass = 0; pass < 4; ++pass) {
+    const int shift = 24 - 8 * pass;
+    const uint32_t himask = pass == 0 ? 0u : (0xFFFFFFFFu << (shift + 8));
+    for (int i = tid; i < QB * 256; i += NTHREADS) hist[i] = 0;
+    __syncthreads();
+    for (int J = tid; J < Nb; J += NTHREADS)
+#pragma unroll
+      for (int r = 0; r < QB; ++r)
+        if (r < nrows) {
+          const uint32_t key = order_key(p[r * Nb + J]);
+          if ((key & himask) == (prefix[r] & himask)) atomicAdd(&hist[r * 256 + ((key >> shift) & 255u)], 1);
+        }
+    __syncthreads();
+    if (wave < nrows) {
+      // lane l holds bins 4l .. 4l+3; find the bin holding the need-th largest
+      const int r = wave;
+      int c[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) c[j] = hist[r * 256 + 4 * lane + j];
+      const int own = c[0] + c[1] + c[2] + c[3];
+      int suffix = own;  // sum over lanes >= lane
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const int y = __shfl_down(suffix, off);
+        if (lane + off < 64) suffix += y;
+      }
+      const int above = suffix - own;
+      const int nd = (int)need[r];
+      if (above < nd && nd <= suffix) {
+        int cum = above;
+#pragma unroll
+        for (int j = 3; j >= 0; --j) {
+          if (cum + c[j] >= nd) {
+            prefix[r] |= (uint32_t)(4 * lane + j) << shift;
+            need[r] = (uint32_t)(nd - cum);
+            neq[r] = (uint32_t)c[j];
+            break;
+          }
+          cum += c[j];
+        }
+      }
+    }
+    __syncthreads();
+  }
+  bool partial = false;  // some row keeps only part of a tie at T
+#pragma unroll
+  for (int r = 0; r < QB; ++r)
+    if (r < nrows && need[r] < neq[r]) partial = true;
+  if (!partial) {
+    for (int J = tid; J < Nb; J += NTHREADS) {
+      int f = 0;
+#pragma unroll
+      for (int r = 0; r < QB; ++r)
+        if (r < nrows && order_key(p[r * Nb + J]) >= prefix[r]) f |= 1 << r;
+      flags[J] = (uint8_t)f;
+    }
+  } else {
+    // contiguous segments per thread, exclusive scan of the count of keys
+    // equal to T: a block equal to T is kept iff fewer than need[r] equal
+    // blocks precede it
+    const int seg = (Nb + NTHREADS - 1) / NTHREADS;
+    const int j0 = min(Nb, tid * seg), j1 = min(Nb, j0 + seg);
+    int cnt[QB];
+#pragma unroll
+    for (int r = 0; r < QB; ++r) {
+      cnt[r] = 0;
+      if (r < nrows)
+        for (int j = j0; j < j1; ++j) cnt[r] += order_key(p[r * Nb + j]) == prefix[r];
+    }
+    int incl[QB];
+#pragma unroll
+    for (int r = 0; r < QB; ++r) {
+      int x = cnt[r];
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const int y = __shfl_up(x, off);
+        if (lane >= off) x += y;
+      }
+      incl[r] = x;
+      if (lane == 63) wsum[r * NW + wave] = x;
+    }
+    __syncthreads();
+    int rank[QB];
+#pragma unroll
+    for (int r = 0; r < QB; ++r) {
+      int base = 0;
+      for (int w = 0; w < wave; ++w) base += wsum[r * NW + w];
+      rank[r] = base + incl[r] - cnt[r];
+    }
+    for (int j = j0; j < j1; ++j) {
+      int f = 0;
+#pragma unroll
+      for (int r = 0; r < QB; ++r) {
+        if (r >= nrows) continue;
+        const uint32_t key = order_key(p[r * Nb + j]);
+        if (key > prefix[r]) {
+          f |= 1 << r;
+        } else if (key == prefix[r]) {
+          if (rank[r] < (int)need[r]) f |= 1 << r;
+          ++rank[r];
+        }
+      }
+      flags[j] = (uint8_t)f;
+    }
+  }
+  if (tid < QB) counts[tid] = tid < nrows ? kk : 0;
+  __syncthreads();
+}
+
 #ifndef SA_XCD_CHUNK
 #define SA_XCD_CHUNK 64
 #endif

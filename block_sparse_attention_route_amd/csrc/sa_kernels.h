@@ -31,6 +31,7 @@ struct RouteArgs {
   const float* kbar;
   int BH, Nb, D;
   float scale, tau;
+  int topk;              // > 0: fixed budget of key blocks per query block
   uint8_t* mask;         // [BH][Nb][Nb]
   int32_t* kept;         // [BH][Nb] or null
 };
@@ -54,6 +55,7 @@ struct AttnArgs {
   int qk_elt, v_elt;
   float scale;           // softmax scale s
   float tau;
+  int topk;              // > 0: fixed budget of key blocks per query block
   int correction;
   bool sparse;           // false: dense attention over all blocks
 };

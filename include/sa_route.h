@@ -14,6 +14,7 @@
  *
  *   pool     qbar_I, kbar_J, vbar_J = means over the tokens of each block
  *   route    p_IJ = s * qbar_I . kbar_J ;  keep_IJ = p_IJ >= max_J p_IJ - tau
+ *            (or, with a fixed budget topk, the topk largest p_IJ of row I)
  *   exact    logits s * q_i . k_j for the tokens j of kept blocks
  *   correct  each skipped J acts as n_J copies of (kbar_J, vbar_J): logit
  *            s * q_i . kbar_J with weight n_J (only if correction != 0)
@@ -53,7 +54,7 @@
 extern "C" {
 #endif
 
-#define SA_ABI_VERSION 1
+#define SA_ABI_VERSION 2
 #define SA_BLOCK 64
 #define SA_MAX_NB 4096
 #define SA_MAX_N (SA_BLOCK * SA_MAX_NB)
@@ -62,7 +63,7 @@ typedef enum sa_status {
   SA_OK = 0,
   SA_ERR_NULL = 1,        /* a required pointer is NULL */
   SA_ERR_SHAPE = 2,       /* bad B/H/N/D, N != T*Hg*Wg, or N > SA_MAX_N */
-  SA_ERR_PARAM = 3,       /* block != 64, tau < 0 or NaN, bad correction flag, bad scale */
+  SA_ERR_PARAM = 3,       /* block != 64, tau < 0 or NaN, topk < 0, bad correction flag, bad scale */
   SA_ERR_DTYPE = 4,       /* unsupported (qk_dtype, v_dtype) pair or scales given/missing */
   SA_ERR_ALIGN = 5,       /* pointer misaligned */
   SA_ERR_WORKSPACE = 6,   /* workspace smaller than sa_workspace_bytes() */
@@ -89,12 +90,19 @@ typedef struct sa_shape {
  * block: must be 64.  tau: threshold below the row maximum of the proxy, in
  * scaled-logit (natural log) units; tau >= 0, +INFINITY keeps every block.
  * correction: 1 = add the skipped-block correction, 0 = drop skipped blocks.
- * scale: softmax scale s; <= 0 selects 1/sqrt(D); must be finite. */
+ * scale: softmax scale s; <= 0 selects 1/sqrt(D); must be finite.
+ * topk: 0 = threshold routing with tau; > 0 = fixed budget instead: every
+ * query block keeps the min(topk, Nb) key blocks of largest proxy, equal
+ * proxies in increasing block order, and tau is ignored (PISA at a fixed
+ * sparsity, paper review of the Sol Video Inference Engine, xllm-io blog:
+ * sparsity f corresponds to topk = ceil((1 - f) * Nb)).  topk < 0 is
+ * SA_ERR_PARAM. */
 typedef struct sa_params {
   int32_t block;
   float tau;
   int32_t correction;
   float scale;
+  int32_t topk;
 } sa_params;
 
 /* Input tensors.  q_scale/k_scale: [B, H, Nb] fp32 block scales, required

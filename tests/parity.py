@@ -67,6 +67,24 @@ def mask_check(inp, b, h, gpu_mask: np.ndarray, tau: float, scale=None):
     return gm, int(band.sum()), int((diff & band).sum())
 
 
+def mask_check_topk(inp, b, h, gpu_mask: np.ndarray, topk: int, scale=None):
+    """Fixed-budget routing: the GPU keeps exactly min(topk, Nb) blocks per
+    query block, and differs from the float64 selection only for blocks whose
+    proxy lies within the band of the row's k-th largest proxy."""
+    q, k, _ = inp.head64(b, h)
+    keep, p, pk = orc.route_topk(q, k, inp.wl.block, topk, scale)
+    gm = gpu_mask.astype(bool)
+    nb = keep.shape[0]
+    assert (gm.sum(axis=1) == min(topk, nb)).all(), "kept count differs from the budget"
+    band = np.abs(p - pk[:, None]) < BAND
+    diff = gm != keep
+    outside = diff & ~band
+    assert not outside.any(), (
+        f"head ({b},{h}): {int(outside.sum())} mask entries differ outside the {BAND} band, "
+        f"first at {np.argwhere(outside)[0].tolist()}")
+    return gm, int(band.sum()), int((diff & band).sum())
+
+
 def output_check(inp, b, h, o_gpu: torch.Tensor, lse_gpu: torch.Tensor, keep: np.ndarray, tau: float,
                  correction: bool, qblocks=None, scale=None, dense=False):
     """Oracle output for the given query blocks of head (b, h) against the GPU's."""

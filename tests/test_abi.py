@@ -35,7 +35,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_abi_version(lib):
-    assert api.sa_abi_version() == 1
+    assert api.sa_abi_version() == 2
 
 
 def test_status_strings(lib):
@@ -52,8 +52,8 @@ def _inputs(qk=api.SA_BF16, v=api.SA_BF16, q=FAKE, k=FAKE, vv=FAKE, qs=None, ks=
     return api.Inputs(q, k, vv, qs, ks, qk, v)
 
 
-def _params(block=64, tau=2.0, corr=1, scale=0.0):
-    return api.Params(block, tau, corr, scale)
+def _params(block=64, tau=2.0, corr=1, scale=0.0, topk=0):
+    return api.Params(block, tau, corr, scale, topk)
 
 
 def _fwd(lib, sh, pr, inp, o=FAKE, lse=FAKE, kept=None, ws=FAKE, ws_bytes=1 << 40):
@@ -96,6 +96,8 @@ def test_bad_shapes(lib, kw, code):
     (dict(tau=math.nan), "SA_ERR_PARAM"),
     (dict(corr=2), "SA_ERR_PARAM"),
     (dict(scale=math.inf), "SA_ERR_PARAM"),
+    (dict(topk=-1), "SA_ERR_PARAM"),
+    (dict(topk=-5, tau=math.nan), "SA_ERR_PARAM"),
 ])
 def test_bad_params(lib, kw, code):
     assert api.status_name(_fwd(lib, _shape(), _params(**kw), _inputs())) == code
@@ -152,3 +154,26 @@ def test_empty_calls_are_ok_without_pointers(lib, kw):
     assert st == 0
     st = lib.sa_dense_forward(ctypes.byref(sh), 0.0, ctypes.byref(inp), None, None, None, 0, None)
     assert st == 0
+
+
+def test_params_struct_layout():
+    # sa_params in include/sa_route.h: block, tau, correction, scale, topk
+    assert ctypes.sizeof(api.Params) == 20
+    assert [f[0] for f in api.Params._fields_] == ["block", "tau", "correction", "scale", "topk"]
+
+
+@pytest.mark.parametrize("sparsity,N,expect", [
+    (0.9, 75600, 119),      # Nb = 1182: ceil(118.2)
+    (0.9, 640, 1),          # Nb = 10: exactly one block
+    (0.75, 512, 2),         # Nb = 8: exactly 2, no rounding up past it
+    (0.0, 1000, 16),        # keep every block
+    (0.99, 64, 1),          # at least one block
+])
+def test_budget_blocks(sparsity, N, expect):
+    assert api.budget_blocks(sparsity, N) == expect
+
+
+@pytest.mark.parametrize("sparsity", [-0.1, 1.0, 1.5])
+def test_budget_blocks_rejects_out_of_range(sparsity):
+    with pytest.raises(ValueError):
+        api.budget_blocks(sparsity, 640)
