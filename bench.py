@@ -2,6 +2,7 @@
 """Benchmark of the on-the-fly block-sparse attention path on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 720p] [--tau 2]
+                    [--budgets 0.9,0.8]
 
 A step is one sa_forward call (pool kernel + fused route/correct/attend
 kernel) over the whole workload, inputs resident in HBM.  Prints one JSON
@@ -13,6 +14,8 @@ covers the fused kernel, timed with HIP events recorded on the stream the
 library launches on, around each launch inside the timed region.  The
 cpu_baseline leg times the float64 CPU oracle on a bounded sample of the same
 workload (a few query blocks of one head) and reports it in the same unit.
+The fixed_budget list times the same call with routing by a fixed number of
+key blocks per query block (sparsity 0.9 and 0.8 by default) instead of tau.
 """
 from __future__ import annotations
 
@@ -50,6 +53,17 @@ def kernel_source_hash() -> str:
         with open(os.path.join(ROOT, "block_sparse_attention_route_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
+
+
+def union_inflation(mask: np.ndarray, group: int = 4) -> float:
+    """Tiles a workgroup of `group` adjacent query blocks streams (the union of
+    their kept lists) over the mean kept count, averaged over the launch."""
+    bh, nb, _ = mask.shape
+    pad = (-nb) % group
+    m = np.concatenate([mask, np.zeros((bh, pad, nb), dtype=mask.dtype)], axis=1) if pad else mask
+    groups = m.reshape(bh, -1, group, nb).astype(bool)
+    union = groups.any(axis=2).sum()
+    return float(union * group) / max(float(mask.astype(bool).sum()), 1.0)
 
 
 def computed_block_flops(mask: np.ndarray, N: int, D: int) -> float:
@@ -124,6 +138,9 @@ def main() -> None:
     ap.add_argument("--dense-steps", type=int, default=2)
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--budgets", default="0.9,0.8",
+                    help="fixed-budget routing sparsities to time as well (comma list, '' for none)")
+    ap.add_argument("--budget-steps", type=int, default=5)
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run one 1 GiB device-to-device copy (reference for the PMC byte counters)")
     args = ap.parse_args()
@@ -234,6 +251,39 @@ def main() -> None:
                  "frac_peak": f_dense / (dms * 1e-3) / 1e12 / peak, "sparse_speedup": dms / ms_step}
         del wsd, od, lsed
 
+    # fixed-budget routing (topk blocks per query block) at the same shape
+    budgets = []
+    ob, lseb = torch.empty_like(o), torch.empty_like(lse)   # keeps o / lse of the tau run intact
+    for sp in [float(x) for x in args.budgets.split(",") if x.strip()]:
+        topk = api.budget_blocks(sp, wl.N)
+        bmask, bkept = api.sa_route(q, k, v, grid, topk=topk, q_scale=qs, k_scale=ks)
+        torch.cuda.synchronize()
+        bmask_np = bmask.cpu().numpy().reshape(wl.B * wl.H, wl.Nb, wl.Nb)
+        del bmask
+        bf = computed_block_flops(bmask_np, wl.N, wl.D)
+
+        def bstep():
+            api.sa_pool(q, k, v, grid, topk=topk, correction=correction, workspace=ws, q_scale=qs, k_scale=ks)
+            api.sa_forward_pooled(q, k, v, grid, topk=topk, correction=correction, workspace=ws, q_scale=qs,
+                                  k_scale=ks, out=ob, lse=lseb, kept=kept, want_kept=True)
+        bstep()
+        torch.cuda.synchronize()
+        assert torch.equal(kept.cpu(), bkept.cpu()), "fused routing disagrees with sa_route (topk)"
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(args.budget_steps):
+            bstep()
+        e1.record()
+        torch.cuda.synchronize()
+        bms = e0.elapsed_time(e1) / args.budget_steps
+        budgets.append({"sparsity": sp, "topk": topk, "ms": bms,
+                        "computed_block_tflops": bf / (bms * 1e-3) / 1e12,
+                        "frac_mfma_peak": bf / (bms * 1e-3) / 1e12 / peak,
+                        "block_density": float(bmask_np.mean()),
+                        "union_inflation": union_inflation(bmask_np),
+                        "speedup_vs_dense": (dense["ms"] / bms) if dense else None})
+        log(f"budget sparsity {sp}: topk {topk}, {bms:.2f} ms")
+
     if args.calibrate_copy:
         src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)
@@ -267,6 +317,7 @@ def main() -> None:
         },
         "frac_mfma_peak": value / peak,
         "block_density": density,
+        "union_inflation": union_inflation(mask_np),
         "work_density": f_exact / f_dense,
         "computed_block_tflop": f_exact / 1e12,
         "correction_tflop": f_corr / 1e12,
@@ -281,6 +332,7 @@ def main() -> None:
                      "kernel": "attn_kernel (fused route + correction + sparse flash attention)",
                      "achieved_incl_correction": (f_exact + f_corr) / (fused_avg * 1e-3) / 1e12},
         "dense": dense,
+        "fixed_budget": budgets,
         "cpu_baseline": cpu,
         "kernel_src": kernel_source_hash(),
     }
