@@ -13,4 +13,5 @@ from .attention import (  # noqa: F401
     proxy_scores,
     route,
     route_topk,
+    tile_order,
 )

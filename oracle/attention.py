@@ -37,7 +37,9 @@ The pages give no formula, so this module fixes the plainest concrete reading
 * alternatively (route_topk) a fixed budget: each query block keeps the topk
   key blocks of largest proxy, equal proxies in increasing block order --
   the paper review of the Sol Video Inference Engine (xllm-io blog) runs
-  PISA at block size 64 and a fixed sparsity rather than a threshold.
+  PISA at block size 64 and a fixed sparsity rather than a threshold;
+* optionally the tokens are first put in 3-D tile order (tile_order): blocks
+  are then cubes of the video token grid rather than raster segments.
 
 It is evaluated here as the two-pass definition above in float64, not as an
 online softmax: first every logit of a row, then its max, then the sums.
@@ -61,6 +63,7 @@ __all__ = [
     "proxy_scores",
     "route",
     "route_topk",
+    "tile_order",
     "attend_rows",
     "forward_head",
     "forward",
@@ -89,6 +92,39 @@ def block_ranges(N: int, block: int) -> list[tuple[int, int]]:
     if block <= 0:
         raise ValueError("block must be positive")
     return [(s, min(s + block, N)) for s in range(0, N, block)]
+
+
+def tile_order(T: int, Hg: int, Wg: int, tile) -> np.ndarray:
+    """Token order that makes blocks 3-D tiles of the video token grid.
+
+    Position -> token index (token n = (t*Hg + y)*Wg + x in the frame-major
+    raster).  First every full tile of tile = (tt, th, tw) tokens, tiles in
+    raster order of their (frame, row, column) tile coordinates and tokens
+    within a tile in (t, y, x) raster order; then every token that no full
+    tile covers, in the raster order.  With tt*th*tw equal to the block size
+    each full tile is exactly one block.  Reading of "3-D tile block ordering
+    from the grid": the Sol-Engine README (section "Sol-Attention") replaces
+    video-token self-attention, whose tokens live on this grid.
+    """
+    tt, th, tw = (int(x) for x in tile)
+    if min(tt, th, tw) < 1:
+        raise ValueError("tile dimensions must be positive")
+    nz, ny, nx = T // tt, Hg // th, Wg // tw
+    order = []
+    for fz in range(nz):
+        for fy in range(ny):
+            for fx in range(nx):
+                for dz in range(tt):
+                    for dy in range(th):
+                        for dx in range(tw):
+                            t, y, x = fz * tt + dz, fy * th + dy, fx * tw + dx
+                            order.append((t * Hg + y) * Wg + x)
+    for t in range(T):
+        for y in range(Hg):
+            for x in range(Wg):
+                if t >= nz * tt or y >= ny * th or x >= nx * tw:
+                    order.append((t * Hg + y) * Wg + x)
+    return np.array(order, dtype=np.int64)
 
 
 def block_means(x: np.ndarray, block: int) -> np.ndarray:
@@ -203,15 +239,27 @@ def attend_rows(q_rows: np.ndarray, k: np.ndarray, v: np.ndarray, keep_row: np.n
 
 def forward_head(q, k, v, block: int = 64, tau: float = math.inf, correction: bool = True,
                  scale: float | None = None, keep: np.ndarray | None = None,
-                 qblocks=None, topk: int | None = None):
+                 qblocks=None, topk: int | None = None, order=None):
     """Sparse attention of one (batch, head): returns (o [N, Dv], lse [N], keep).
 
     keep: optional externally supplied [Nb, Nb] mask replacing the routing
     (used to evaluate the definition on a mask that differs from this oracle's
     only inside the near-threshold band).  qblocks: optional iterable of query
     block indices; rows of other blocks are left as NaN.  topk: route with the
-    fixed budget of route_topk() instead of the threshold tau.
+    fixed budget of route_topk() instead of the threshold tau.  order:
+    optional position -> token permutation (tile_order()); blocks are then
+    formed over the permuted tokens, keep and qblocks index those blocks, and
+    o / lse are returned in the original token order.
     """
+    if order is not None:
+        order = np.asarray(order)
+        o_p, lse_p, keep = forward_head(np.asarray(q)[order], np.asarray(k)[order], np.asarray(v)[order],
+                                        block, tau, correction, scale, keep, qblocks, topk)
+        o = np.empty_like(o_p)
+        lse = np.empty_like(lse_p)
+        o[order] = o_p
+        lse[order] = lse_p
+        return o, lse, keep
     q = np.asarray(q, dtype=np.float64)
     N = q.shape[0]
     if keep is None:
@@ -229,7 +277,7 @@ def forward_head(q, k, v, block: int = 64, tau: float = math.inf, correction: bo
 
 
 def forward(q, k, v, block: int = 64, tau: float = math.inf, correction: bool = True,
-            scale: float | None = None, topk: int | None = None):
+            scale: float | None = None, topk: int | None = None, order=None):
     """[B, H, N, D] batched form of forward_head; every (b, h) routes independently."""
     q = np.asarray(q, dtype=np.float64)
     B, H, N, _ = q.shape
@@ -239,7 +287,7 @@ def forward(q, k, v, block: int = 64, tau: float = math.inf, correction: bool = 
     for b in range(B):
         for h in range(H):
             o[b, h], lse[b, h], keep[b, h] = forward_head(q[b, h], k[b, h], v[b, h], block, tau,
-                                                          correction, scale, topk=topk)
+                                                          correction, scale, topk=topk, order=order)
     return o, lse, keep
 
 

@@ -15,6 +15,7 @@ import numpy as np
 import pytest
 
 from tests import test_oracle_pins as pins
+from tests import test_oracle_tiles as tile_pins
 from tests import test_oracle_topk as topk_pins
 
 SRC = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "oracle", "attention.py")
@@ -41,6 +42,13 @@ MUTANTS = {
     "topk_smallest_proxies": (
         "order = np.lexsort((np.arange(nb), -p[I]))", "order = np.lexsort((np.arange(nb), p[I]))"),
     "topk_one_short": ("keep[I, order[:kk]] = True", "keep[I, order[:max(kk - 1, 1)]] = True"),
+    "tile_inner_order_transposed": (
+        "t, y, x = fz * tt + dz, fy * th + dy, fx * tw + dx",
+        "t, y, x = fz * tt + (dx % tt), fy * th + dy, fx * tw + (dz % tw)"),
+    "tile_leftovers_dropped_to_raster": (
+        "if t >= nz * tt or y >= ny * th or x >= nx * tw:",
+        "if t >= nz * tt and y >= ny * th and x >= nx * tw:"),
+    "tile_outputs_not_scattered_back": ("        o[order] = o_p\n", "        o[:] = o_p[order]\n"),
 }
 
 
@@ -69,12 +77,18 @@ def _pins_pass(mod) -> bool:
         topk_pins.test_topk_brute_force_with_ties()
         for topk in (1, 2, 3):
             topk_pins.test_topk_brute_force_tiny(12, 4, 3, topk, True)
+        tile_pins.orc = mod
+        for case in tile_pins._cases():
+            tile_pins.test_hand_written_orders(case)
+        tile_pins.test_tile_constant_kv_is_exact(0.0)
+        tile_pins.test_brute_force_over_tiled_blocks(0.5, None, True)
         return True
     except AssertionError:
         return False
     finally:
         pins.orc = saved
         topk_pins.orc = saved
+        tile_pins.orc = saved
 
 
 def _source() -> str:
