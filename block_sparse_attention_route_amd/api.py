@@ -52,7 +52,8 @@ class Shape(ctypes.Structure):
 class Params(ctypes.Structure):
     _fields_ = [("block", ctypes.c_int32), ("tau", ctypes.c_float),
                 ("correction", ctypes.c_int32), ("scale", ctypes.c_float),
-                ("topk", ctypes.c_int32)]
+                ("topk", ctypes.c_int32),
+                ("tile_t", ctypes.c_int32), ("tile_h", ctypes.c_int32), ("tile_w", ctypes.c_int32)]
 
 
 class Inputs(ctypes.Structure):
@@ -82,6 +83,8 @@ def load_library():
     lib.sa_status_string.argtypes = [st]
     lib.sa_last_error.restype = ctypes.c_char_p
     lib.sa_last_error.argtypes = []
+    lib.sa_last_status.restype = st
+    lib.sa_last_status.argtypes = []
     lib.sa_workspace_bytes.restype = sz
     lib.sa_workspace_bytes.argtypes = [P, S, I]
     lib.sa_dense_workspace_bytes.restype = sz
@@ -130,8 +133,10 @@ def make_shape(q: torch.Tensor, grid) -> Shape:
     return Shape(B, H, N, D, T, Hg, Wg)
 
 
-def make_params(tau: float, correction: bool = True, scale: float = 0.0, topk: int = 0) -> Params:
-    return Params(BLOCK, float(tau), int(bool(correction)), float(scale), int(topk))
+def make_params(tau: float, correction: bool = True, scale: float = 0.0, topk: int = 0,
+                tile=None) -> Params:
+    tt, th, tw = (0, 0, 0) if tile is None else (int(x) for x in tile)
+    return Params(BLOCK, float(tau), int(bool(correction)), float(scale), int(topk), tt, th, tw)
 
 
 def budget_blocks(sparsity: float, N: int) -> int:
@@ -158,13 +163,14 @@ def sa_abi_version() -> int:
     return int(load_library().sa_abi_version())
 
 
-def sa_workspace_bytes(q, k, v, grid, q_scale=None, k_scale=None) -> int:
+def sa_workspace_bytes(q, k, v, grid, q_scale=None, k_scale=None, tile=None) -> int:
     lib = load_library()
     sh = make_shape(q, grid)
     inp = Inputs(None, None, None, None, None, _dtype_code(q), _dtype_code(v))
-    n = lib.sa_workspace_bytes(ctypes.byref(sh), None, ctypes.byref(inp))
+    pr = make_params(math.inf, True, 0.0, 0, tile)
+    n = lib.sa_workspace_bytes(ctypes.byref(sh), ctypes.byref(pr), ctypes.byref(inp))
     if n == 0 and sh.B * sh.H * sh.N > 0:
-        raise SaError(1, lib.sa_last_error().decode() or "invalid arguments")
+        raise SaError(int(lib.sa_last_status()), lib.sa_last_error().decode() or "invalid arguments")
     return int(n)
 
 
@@ -182,27 +188,28 @@ def _workspace(nbytes: int, like: torch.Tensor, ws: torch.Tensor | None) -> torc
 
 
 def sa_pool(q, k, v, grid, *, tau: float = math.inf, correction: bool = True, scale: float = 0.0,
-            workspace: torch.Tensor | None = None, q_scale=None, k_scale=None, topk: int = 0) -> torch.Tensor:
+            workspace: torch.Tensor | None = None, q_scale=None, k_scale=None, topk: int = 0,
+            tile=None) -> torch.Tensor:
     """Step pool: block means (and V regrouped per 64-key block) into the workspace."""
     lib = load_library()
-    ws = _workspace(sa_workspace_bytes(q, k, v, grid, q_scale, k_scale), q, workspace)
-    sh, pr, inp = make_shape(q, grid), make_params(tau, correction, scale, topk), make_inputs(q, k, v, q_scale, k_scale)
+    ws = _workspace(sa_workspace_bytes(q, k, v, grid, q_scale, k_scale, tile), q, workspace)
+    sh, pr, inp = make_shape(q, grid), make_params(tau, correction, scale, topk, tile), make_inputs(q, k, v, q_scale, k_scale)
     _check(lib.sa_pool(ctypes.byref(sh), ctypes.byref(pr), ctypes.byref(inp), _ptr(ws), ws.numel(), _stream(q)))
     return ws
 
 
 def sa_route(q, k, v, grid, *, tau: float = math.inf, scale: float = 0.0, workspace=None, q_scale=None,
-             k_scale=None, mask=None, kept=None, topk: int = 0):
+             k_scale=None, mask=None, kept=None, topk: int = 0, tile=None):
     """Steps pool + route: returns (mask uint8 [B,H,Nb,Nb], kept int32 [B,H,Nb])."""
     lib = load_library()
     B, H, N, _ = q.shape
     Nb = _nb(N)
-    ws = _workspace(sa_workspace_bytes(q, k, v, grid, q_scale, k_scale), q, workspace)
+    ws = _workspace(sa_workspace_bytes(q, k, v, grid, q_scale, k_scale, tile), q, workspace)
     if mask is None:
         mask = torch.empty((B, H, Nb, Nb), dtype=torch.uint8, device=q.device)
     if kept is None:
         kept = torch.empty((B, H, Nb), dtype=torch.int32, device=q.device)
-    sh, pr, inp = make_shape(q, grid), make_params(tau, True, scale, topk), make_inputs(q, k, v, q_scale, k_scale)
+    sh, pr, inp = make_shape(q, grid), make_params(tau, True, scale, topk, tile), make_inputs(q, k, v, q_scale, k_scale)
     _check(lib.sa_route(ctypes.byref(sh), ctypes.byref(pr), ctypes.byref(inp), _ptr(mask), _ptr(kept),
                         _ptr(ws), ws.numel(), _stream(q)))
     return mask, kept
@@ -221,12 +228,12 @@ def _outs(q, v, out, lse, want_kept, kept):
 
 def sa_forward(q, k, v, grid, *, tau: float = math.inf, correction: bool = True, scale: float = 0.0,
                workspace=None, q_scale=None, k_scale=None, out=None, lse=None, want_kept=False,
-               kept=None, topk: int = 0):
+               kept=None, topk: int = 0, tile=None):
     """Pool + fused routed sparse attention with correction: returns (o, lse, kept or None)."""
     lib = load_library()
-    ws = _workspace(sa_workspace_bytes(q, k, v, grid, q_scale, k_scale), q, workspace)
+    ws = _workspace(sa_workspace_bytes(q, k, v, grid, q_scale, k_scale, tile), q, workspace)
     out, lse, kept = _outs(q, v, out, lse, want_kept, kept)
-    sh, pr, inp = make_shape(q, grid), make_params(tau, correction, scale, topk), make_inputs(q, k, v, q_scale, k_scale)
+    sh, pr, inp = make_shape(q, grid), make_params(tau, correction, scale, topk, tile), make_inputs(q, k, v, q_scale, k_scale)
     _check(lib.sa_forward(ctypes.byref(sh), ctypes.byref(pr), ctypes.byref(inp), _ptr(out), _ptr(lse),
                           _ptr(kept), _ptr(ws), ws.numel(), _stream(q)))
     return out, lse, kept
@@ -234,11 +241,11 @@ def sa_forward(q, k, v, grid, *, tau: float = math.inf, correction: bool = True,
 
 def sa_forward_pooled(q, k, v, grid, *, tau: float = math.inf, correction: bool = True, scale: float = 0.0,
                       workspace, q_scale=None, k_scale=None, out=None, lse=None, want_kept=False,
-                      kept=None, topk: int = 0):
+                      kept=None, topk: int = 0, tile=None):
     """The fused kernel alone; `workspace` must hold sa_pool's output for these inputs."""
     lib = load_library()
     out, lse, kept = _outs(q, v, out, lse, want_kept, kept)
-    sh, pr, inp = make_shape(q, grid), make_params(tau, correction, scale, topk), make_inputs(q, k, v, q_scale, k_scale)
+    sh, pr, inp = make_shape(q, grid), make_params(tau, correction, scale, topk, tile), make_inputs(q, k, v, q_scale, k_scale)
     _check(lib.sa_forward_pooled(ctypes.byref(sh), ctypes.byref(pr), ctypes.byref(inp), _ptr(out), _ptr(lse),
                                  _ptr(kept), _ptr(workspace), workspace.numel(), _stream(q)))
     return out, lse, kept

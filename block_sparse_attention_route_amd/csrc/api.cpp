@@ -18,17 +18,20 @@
 namespace {
 
 thread_local char g_err[512] = "";
+thread_local sa_status g_status = SA_OK;
 
 sa_status fail(sa_status s, const char* fmt, ...) {
   va_list ap;
   va_start(ap, fmt);
   vsnprintf(g_err, sizeof(g_err), fmt, ap);
   va_end(ap);
+  g_status = s;
   return s;
 }
 
 sa_status ok() {
   g_err[0] = '\0';
+  g_status = SA_OK;
   return SA_OK;
 }
 
@@ -42,6 +45,9 @@ struct Req {
   float scale, tau;
   int topk;
   int correction;
+  int T, Hg, Wg;
+  bool dense;
+  sa::TileMap tm;
   sa::WsLayout ws;
 };
 
@@ -71,6 +77,11 @@ sa_status check_shape_inputs(const sa_shape* sh, const sa_inputs* in, Req* r, bo
   r->qk = qk;
   r->v = v;
   r->empty = r->BH * r->N == 0;
+  r->T = sh->T;
+  r->Hg = sh->Hg;
+  r->Wg = sh->Wg;
+  r->dense = dense;
+  r->tm = sa::make_tile_map(sh->T, sh->Hg, sh->Wg, 0, 0, 0);
   if (r->BH > (int64_t)1 << 24) return fail(SA_ERR_SHAPE, "B*H too large");
   r->ws = sa::ws_layout(r->BH, r->N, r->D, v == SA_BF16, dense);
   if (!ptrs) return SA_OK;  // sizing only: data pointers are not needed
@@ -95,6 +106,17 @@ sa_status check_params(const sa_params* p, Req* r) {
     return fail(SA_ERR_PARAM, "tau must be >= 0 or +inf");
   if (p->correction != 0 && p->correction != 1) return fail(SA_ERR_PARAM, "correction must be 0 or 1");
   if (!std::isfinite(p->scale)) return fail(SA_ERR_PARAM, "scale must be finite");
+  const int tt = p->tile_t, th = p->tile_h, tw = p->tile_w;
+  if (tt != 0 || th != 0 || tw != 0) {
+    if (tt < 1 || th < 1 || tw < 1 || (int64_t)tt * th * tw != SA_BLOCK)
+      return fail(SA_ERR_PARAM, "tile (%d, %d, %d) must be all 0 or positive with product %d", tt, th, tw,
+                  SA_BLOCK);
+    if (r->qk == SA_FP8_E4M3)
+      return fail(SA_ERR_UNSUPPORTED, "a 3-D tile order needs bf16 or fp32 Q/K (fp8 block scales "
+                  "belong to raster blocks)");
+    r->tm = sa::make_tile_map(r->T, r->Hg, r->Wg, tt, th, tw);
+    r->ws = sa::ws_layout(r->BH, r->N, r->D, r->v == SA_BF16, r->dense, true);
+  }
   r->tau = p->tau;
   r->topk = p->topk;
   r->correction = p->correction;
@@ -149,6 +171,10 @@ sa::PoolArgs pool_args(const Req& r, const sa_inputs* in, void* ws, bool vt_only
     }
   }
   if (r.v == SA_BF16) a.vt16 = at<uint16_t>(ws, r.ws.vt16);
+  if (!vt_only) {
+    a.tm = r.tm;
+    if (r.tm.on && r.qk == SA_BF16) a.kpos16 = at<uint16_t>(ws, r.ws.kpos16);
+  }
   return a;
 }
 
@@ -170,6 +196,10 @@ sa::AttnArgs attn_args(const Req& r, const sa_inputs* in, void* o, float* lse, i
     }
   }
   if (r.v == SA_BF16) a.vt16 = at<uint16_t>(ws, r.ws.vt16);
+  if (sparse) {
+    a.tm = r.tm;
+    if (r.tm.on && r.qk == SA_BF16) a.kpos16 = at<uint16_t>(ws, r.ws.kpos16);
+  }
   a.o = o;
   a.lse = lse;
   a.kept = kept;
@@ -221,18 +251,22 @@ SA_API const char* sa_status_string(sa_status s) {
 
 SA_API const char* sa_last_error(void) { return g_err; }
 
+SA_API sa_status sa_last_status(void) { return g_status; }
+
 SA_API size_t sa_workspace_bytes(const sa_shape* shape, const sa_params* params, const sa_inputs* in) {
   Req r{};
   if (check_shape_inputs(shape, in, &r, false, false) != SA_OK) return 0;
   if (params) {
     if (check_params(params, &r) != SA_OK) return 0;
   }
+  ok();
   return r.ws.total;
 }
 
 SA_API size_t sa_dense_workspace_bytes(const sa_shape* shape, const sa_inputs* in) {
   Req r{};
   if (check_shape_inputs(shape, in, &r, true, false) != SA_OK) return 0;
+  ok();
   return r.ws.total;
 }
 

@@ -49,9 +49,10 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(AttnArgs a) {
     if (a.kept && lane == 0) a.kept[(size_t)bh * Nb + I] = counts[0];
   }
 
-  const int row = I * kBlock + lane;
+  const int row = I * kBlock + lane;   // position; its token is token_of(row)
   const bool rv = row < N;
-  const float* qsrc = reinterpret_cast<const float*>(a.q) + ((size_t)bh * N + row) * D;
+  const size_t tok = (size_t)bh * N + (rv ? token_of(a.tm, row) : row);
+  const float* qsrc = reinterpret_cast<const float*>(a.q) + tok * D;
   float q[D], acc[D];
 #pragma unroll
   for (int d = 0; d < D; ++d) {
@@ -126,9 +127,19 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(AttnArgs a) {
   for (int J = 0; J < Nb; ++J) {
     if (SPARSE && !(flags[J] & 1)) continue;
     const int n = min(kBlock, N - J * kBlock);
-    for (int x = lane; x < n * D; x += 64) {
-      kt[x] = kin[(size_t)J * kBlock * D + x];
-      vt[x] = vin[(size_t)J * kBlock * D + x];
+    if (a.tm.on) {
+      for (int r = 0; r < n; ++r) {
+        const size_t t = (size_t)token_of(a.tm, J * kBlock + r) * D;
+        for (int d = lane; d < D; d += 64) {
+          kt[r * D + d] = kin[t + d];
+          vt[r * D + d] = vin[t + d];
+        }
+      }
+    } else {
+      for (int x = lane; x < n * D; x += 64) {
+        kt[x] = kin[(size_t)J * kBlock * D + x];
+        vt[x] = vin[(size_t)J * kBlock * D + x];
+      }
     }
     if (lane < n) lw[lane] = 0.f;
     __syncthreads();
@@ -138,10 +149,10 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(AttnArgs a) {
 
   if (rv) {
     const float inv = 1.f / l;
-    float* orow = reinterpret_cast<float*>(a.o) + ((size_t)bh * N + row) * D;
+    float* orow = reinterpret_cast<float*>(a.o) + tok * D;
 #pragma unroll
     for (int d = 0; d < D; ++d) orow[d] = acc[d] * inv;
-    a.lse[(size_t)bh * N + row] = m + logf(l);
+    a.lse[tok] = m + logf(l);
   }
 }
 

@@ -248,7 +248,8 @@ __global__ __launch_bounds__(128 * QB, QB == 2 ? 2 : 1) void attn_kernel(AttnArg
   // --------------------------------------- query operands (B of S^T = K Q^T)
   const int qrow = I * kBlock + 32 * qhalf + l32;  // this lane's query row
   const bool rowvalid = qvalid && qrow < N;
-  const size_t qtok = (size_t)bh * N + qrow;
+  // position qrow holds token token_of(qrow): the raster order, or the 3-D tile order
+  const size_t qtok = (size_t)bh * N + (rowvalid ? token_of(a.tm, qrow) : qrow);
   bf16x8 qr[C::KS];
   uint64_t q8[FP8 ? C::KS : 1];
 #pragma unroll
@@ -297,7 +298,9 @@ __global__ __launch_bounds__(128 * QB, QB == 2 ? 2 : 1) void attn_kernel(AttnArg
     } else {
       const int J = tile_block(it);
       k8 = FP8;
-      ksrc = reinterpret_cast<const uint8_t*>(a.k) + ((size_t)bh * N + (size_t)J * kBlock) * D * (FP8 ? 1 : 2);
+      // keys in position order: the caller's K, or its copy in tile order
+      const void* kpos = (!FP8 && a.tm.on) ? static_cast<const void*>(a.kpos16) : a.k;
+      ksrc = reinterpret_cast<const uint8_t*>(kpos) + ((size_t)bh * N + (size_t)J * kBlock) * D * (FP8 ? 1 : 2);
       vsrc = reinterpret_cast<const uint8_t*>(a.vt16 + ((size_t)bh * Nb + J) * D * kBlock);
       kvalid = min(kBlock, N - J * kBlock);
     }

@@ -4,7 +4,9 @@
 //
 // The Sol-Attn project page (section "Abstract") routes on a pooled score;
 // this library reads "pooled" as the mean over each 64-token block's actual
-// tokens.  The kernel is HBM-bound: it reads Q, K and V once (each workgroup
+// tokens.  Blocks are taken over positions: the raster order, or the 3-D
+// tile order of the token grid (sa_layout.h, token_of), in which case K is
+// also written out in position order.  The kernel is HBM-bound: it reads Q, K and V once (each workgroup
 // one 64-token block of one head, all three tensors in flight together) and
 // writes 1/16 as many bytes of means plus the regrouped V.
 //
@@ -56,16 +58,21 @@ __device__ __forceinline__ void unpack(const u32x4& c, float* out) {
   }
 }
 
+// Rows pos0 .. pos0 + nrows - 1 of the block, in position order: row r is
+// token token_of(tm, pos0 + r) of the head whose tokens start at `head`.
 template <int E, int D>
-__device__ __forceinline__ void load_block(const uint8_t* __restrict__ base, int nrows,
-                                           u32x4 (&raw)[Tiling<E, D>::P]) {
+__device__ __forceinline__ void load_block(const uint8_t* __restrict__ head, int pos0, int nrows,
+                                           const TileMap& tm, u32x4 (&raw)[Tiling<E, D>::P]) {
   using T = Tiling<E, D>;
   const int c = threadIdx.x % T::CPR, g = threadIdx.x / T::CPR;
 #pragma unroll
   for (int i = 0; i < T::P; ++i) {
     const int r = g + T::G * i;
     raw[i] = u32x4{0u, 0u, 0u, 0u};
-    if (r < nrows) raw[i] = *reinterpret_cast<const u32x4*>(base + ((size_t)r * D * T::B) + c * 16);
+    if (r < nrows) {
+      const size_t tok = (size_t)token_of(tm, pos0 + r);
+      raw[i] = *reinterpret_cast<const u32x4*>(head + tok * D * T::B + c * 16);
+    }
   }
 }
 
@@ -108,7 +115,7 @@ __global__ __launch_bounds__(256) void pool_kernel(PoolArgs a) {
   const int bh = blockIdx.y;
   const int row0 = J * kBlock;
   const int nrows = min(kBlock, a.N - row0);
-  const size_t tok0 = (size_t)bh * a.N + row0;
+  const size_t head0 = (size_t)bh * a.N;
 
   __shared__ float part[4096];  // up to 64 row groups x 64 dims or 32 x 128
   __shared__ __attribute__((aligned(16))) uint16_t vtl[D * kBlock];
@@ -116,11 +123,26 @@ __global__ __launch_bounds__(256) void pool_kernel(PoolArgs a) {
   using TQ = Tiling<QE, D>;
   using TV = Tiling<VE, D>;
   u32x4 rq[TQ::P], rk[TQ::P], rv[TV::P];
+  const TileMap tm = a.tm;
   if constexpr (!VT_ONLY) {
-    load_block<QE, D>(reinterpret_cast<const uint8_t*>(a.q) + tok0 * D * TQ::B, nrows, rq);
-    load_block<QE, D>(reinterpret_cast<const uint8_t*>(a.k) + tok0 * D * TQ::B, nrows, rk);
+    load_block<QE, D>(reinterpret_cast<const uint8_t*>(a.q) + head0 * D * TQ::B, row0, nrows, tm, rq);
+    load_block<QE, D>(reinterpret_cast<const uint8_t*>(a.k) + head0 * D * TQ::B, row0, nrows, tm, rk);
   }
-  load_block<VE, D>(reinterpret_cast<const uint8_t*>(a.v) + tok0 * D * TV::B, nrows, rv);
+  load_block<VE, D>(reinterpret_cast<const uint8_t*>(a.v) + head0 * D * TV::B, row0, nrows, tm, rv);
+
+  if constexpr (!VT_ONLY && QE == ELT_BF16) {
+    // 3-D tile order: K also in position order, for the attention kernel's
+    // contiguous tile copies
+    if (tm.on) {
+      const int c = threadIdx.x % TQ::CPR, g = threadIdx.x / TQ::CPR;
+      uint8_t* dst = reinterpret_cast<uint8_t*>(a.kpos16) + (head0 + row0) * D * 2;
+#pragma unroll
+      for (int i = 0; i < TQ::P; ++i) {
+        const int r = g + TQ::G * i;
+        if (r < nrows) *reinterpret_cast<u32x4*>(dst + (size_t)r * D * 2 + c * 16) = rk[i];
+      }
+    }
+  }
 
   const size_t mrow = ((size_t)bh * a.Nb + J) * D;
   if constexpr (!VT_ONLY) {

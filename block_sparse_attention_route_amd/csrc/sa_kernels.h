@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "sa_layout.h"
+
 namespace sa {
 
 enum Elt : int { ELT_F32 = 0, ELT_BF16 = 1, ELT_FP8 = 2 };
@@ -24,6 +26,8 @@ struct PoolArgs {
   uint16_t* kbar16;
   uint16_t* vbarT16;
   uint16_t* vt16;
+  TileMap tm;            // position -> token order (on == 0: raster)
+  uint16_t* kpos16;      // K in position order, written when tm.on (bf16 K)
 };
 
 struct RouteArgs {
@@ -48,6 +52,8 @@ struct AttnArgs {
   const uint16_t* kbar16;
   const uint16_t* vbarT16;
   const uint16_t* vt16;
+  TileMap tm;            // position -> token order (on == 0: raster)
+  const uint16_t* kpos16;  // K in position order when tm.on (bf16 K)
   void* o;
   float* lse;
   int32_t* kept;

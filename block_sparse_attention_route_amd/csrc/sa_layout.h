@@ -9,8 +9,11 @@
 //                                     time and transposed, cols >= Nb zero (bf16 V only)
 //   vt16    bf16  [BH][Nb][D][64]     V regrouped per 64-key block and
 //                                     transposed (d-major), keys >= N zero (bf16 V only)
+//   kpos16  bf16  [BH][N][D]          K in block (position) order; only with a
+//                                     3-D tile order (bf16 K only)
 //
-// The dense path uses only vt16.
+// The dense path uses only vt16.  Blocks are formed over positions: position
+// i is token i in the raster order, or token_of(i) in the 3-D tile order.
 #pragma once
 
 #include <stddef.h>
@@ -22,13 +25,73 @@ constexpr int kBlock = 64;
 constexpr int kMaxNb = 4096;
 
 struct WsLayout {
-  size_t qbar, kbar, vbar, kbar16, vbarT16, vt16, total;
+  size_t qbar, kbar, vbar, kbar16, vbarT16, vt16, kpos16, total;
 };
+
+// Position -> token map of the 3-D tile order.  Full tiles of tt x th x tw =
+// 64 tokens come first, in raster order of their (frame, row, column) tile
+// coordinates, tokens inside a tile in (t, y, x) raster order; then every
+// token outside the full tiles, in the frame-major raster order.  on == 0 is
+// the raster order itself.  Filled on the host (make_tile_map).
+struct TileMap {
+  int on;
+  int Hg, Wg;        // grid rows and columns of a frame
+  int tt, th, tw;    // tile extent, tt * th * tw == 64
+  int nfy, nfx;      // full tiles along y and x
+  int nfull;         // full tiles in total
+  int Tf, Hf, Wf;    // extent covered by full tiles
+};
+
+__host__ __device__ inline TileMap make_tile_map(int T, int Hg, int Wg, int tt, int th, int tw) {
+  TileMap m{};
+  m.on = (tt > 0) ? 1 : 0;
+  m.Hg = Hg;
+  m.Wg = Wg;
+  m.tt = tt > 0 ? tt : 1;
+  m.th = th > 0 ? th : 1;
+  m.tw = tw > 0 ? tw : 1;
+  m.nfy = Hg / m.th;
+  m.nfx = Wg / m.tw;
+  const int nfz = T / m.tt;
+  m.nfull = nfz * m.nfy * m.nfx;
+  m.Tf = nfz * m.tt;
+  m.Hf = m.nfy * m.th;
+  m.Wf = m.nfx * m.tw;
+  return m;
+}
+
+// Token index (within one head) at position pos.
+__host__ __device__ inline int token_of(const TileMap& m, int pos) {
+  if (!m.on) return pos;
+  if (pos < 64 * m.nfull) {
+    const int f = pos >> 6, w = pos & 63;
+    const int fx = f % m.nfx, fy = (f / m.nfx) % m.nfy, fz = f / (m.nfx * m.nfy);
+    const int dx = w % m.tw, dy = (w / m.tw) % m.th, dz = w / (m.tw * m.th);
+    return ((fz * m.tt + dz) * m.Hg + fy * m.th + dy) * m.Wg + fx * m.tw + dx;
+  }
+  const int r = pos - 64 * m.nfull;           // rank among the uncovered tokens
+  const int wl = m.Wg - m.Wf;                 // uncovered columns of a covered row
+  const int lf = m.Hf * wl + (m.Hg - m.Hf) * m.Wg;  // uncovered tokens of a frame t < Tf
+  if (r < m.Tf * lf) {
+    const int t = r / lf, r2 = r - t * lf;
+    int y, x;
+    if (r2 < m.Hf * wl) {
+      y = r2 / wl;
+      x = m.Wf + r2 % wl;
+    } else {
+      const int r3 = r2 - m.Hf * wl;
+      y = m.Hf + r3 / m.Wg;
+      x = r3 % m.Wg;
+    }
+    return (t * m.Hg + y) * m.Wg + x;
+  }
+  return m.Tf * m.Hg * m.Wg + (r - m.Tf * lf);   // frames t >= Tf: all of them
+}
 
 __host__ __device__ inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 __host__ __device__ inline WsLayout ws_layout(int64_t BH, int64_t N, int64_t D, bool v_bf16,
-                                              bool dense_only) {
+                                              bool dense_only, bool tiled = false) {
   const int64_t Nb = (N + kBlock - 1) / kBlock;
   const int64_t Nbp = (Nb + 63) / 64 * 64;
   WsLayout L{};
@@ -48,6 +111,7 @@ __host__ __device__ inline WsLayout ws_layout(int64_t BH, int64_t N, int64_t D, 
     }
   }
   if (v_bf16) L.vt16 = take((size_t)(BH * Nb * D * kBlock) * 2);
+  if (tiled && v_bf16 && !dense_only) L.kpos16 = take((size_t)(BH * N * D) * 2);
   L.total = off;
   return L;
 }

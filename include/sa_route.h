@@ -54,7 +54,7 @@
 extern "C" {
 #endif
 
-#define SA_ABI_VERSION 2
+#define SA_ABI_VERSION 3
 #define SA_BLOCK 64
 #define SA_MAX_NB 4096
 #define SA_MAX_N (SA_BLOCK * SA_MAX_NB)
@@ -96,13 +96,25 @@ typedef struct sa_shape {
  * proxies in increasing block order, and tau is ignored (PISA at a fixed
  * sparsity, paper review of the Sol Video Inference Engine, xllm-io blog:
  * sparsity f corresponds to topk = ceil((1 - f) * Nb)).  topk < 0 is
- * SA_ERR_PARAM. */
+ * SA_ERR_PARAM.
+ * tile_t, tile_h, tile_w: 0, 0, 0 = blocks are 64 consecutive tokens of the
+ * raster order.  Otherwise (each >= 1, product 64) blocks are formed over the
+ * tokens in 3-D tile order: first every full tile_t x tile_h x tile_w tile of
+ * the grid, tiles in raster order of their tile coordinates and tokens inside
+ * a tile in (t, y, x) order, then the tokens no full tile covers, in raster
+ * order; so every full tile is one block.  Masks, kept counts and the
+ * means index these blocks; O and LSE stay in the caller's token order.
+ * Needs bf16 or fp32 Q/K (fp8 block scales belong to raster blocks:
+ * SA_ERR_UNSUPPORTED); the workspace grows by a copy of K in tile order.
+ * Reading of video-token blocks on the grid (Sol-Engine README,
+ * "Sol-Attention"). */
 typedef struct sa_params {
   int32_t block;
   float tau;
   int32_t correction;
   float scale;
   int32_t topk;
+  int32_t tile_t, tile_h, tile_w;
 } sa_params;
 
 /* Input tensors.  q_scale/k_scale: [B, H, Nb] fp32 block scales, required
@@ -127,6 +139,10 @@ const char* sa_status_string(sa_status s);
 /* Detail of the last failed call made by this thread (static per thread;
  * empty string if none). */
 const char* sa_last_error(void);
+
+/* Status of the last call made by this thread (SA_OK after a successful
+ * call): the reason when a size query below returns 0. */
+sa_status sa_last_status(void);
 
 /* Workspace bytes that sa_pool / sa_route / sa_forward / sa_forward_pooled
  * need for this shape and dtypes (block means in fp32, bf16 copies of the

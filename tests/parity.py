@@ -25,9 +25,16 @@ import torch
 from oracle import attention as orc
 
 BAND = 1e-3
+# O tolerances are the stated bars (fp32: row-normwise relative 1e-5; bf16: max
+# abs 2e-2, mean abs 2e-3; fp8: max abs 4e-2).  LSE has no stated bar; ours is
+# derived from the arithmetic: the bf16 paths round P to bf16 (relative 2^-9
+# per weight) and the correction operands kbar, vbar to bf16, so a correction
+# logit s*q.kbar carries up to 2^-9 * s*|q||kbar|, about 1e-2 at the logit
+# scale of these workloads, and it enters the LSE with the (dominant, when few
+# blocks are kept) weight of the skipped blocks: 2e-2 for bf16 and fp8.
 TOL = {
     "f32": dict(row_rel=1e-5, lse_rel=1e-5),
-    "bf16": dict(max_abs=2e-2, mean_abs=2e-3, lse_abs=1e-2),
+    "bf16": dict(max_abs=2e-2, mean_abs=2e-3, lse_abs=2e-2),
     "fp8": dict(max_abs=4e-2, lse_abs=2e-2),
 }
 
@@ -47,12 +54,20 @@ def grid_of(wl):
     return (wl.T, wl.Hg, wl.Wg)
 
 
-def mask_check(inp, b, h, gpu_mask: np.ndarray, tau: float, scale=None):
+def _head(inp, b, h, order):
+    q, k, v = inp.head64(b, h)
+    if order is not None:
+        q, k, v = q[order], k[order], v[order]
+    return q, k, v
+
+
+def mask_check(inp, b, h, gpu_mask: np.ndarray, tau: float, scale=None, order=None):
     """Compare the GPU keep mask of one head with the float64 routing.
 
     Returns (keep_for_oracle, n_band, n_flipped_in_band); asserts that no block
-    outside the near-threshold band differs."""
-    q, k, _ = inp.head64(b, h)
+    outside the near-threshold band differs.  order: position -> token map of
+    the blocks (3-D tile order), None for the raster order."""
+    q, k, _ = _head(inp, b, h, order)
     keep, p, m = orc.route(q, k, inp.wl.block, tau, scale)
     gm = gpu_mask.astype(bool)
     if math.isinf(tau):
@@ -67,11 +82,11 @@ def mask_check(inp, b, h, gpu_mask: np.ndarray, tau: float, scale=None):
     return gm, int(band.sum()), int((diff & band).sum())
 
 
-def mask_check_topk(inp, b, h, gpu_mask: np.ndarray, topk: int, scale=None):
+def mask_check_topk(inp, b, h, gpu_mask: np.ndarray, topk: int, scale=None, order=None):
     """Fixed-budget routing: the GPU keeps exactly min(topk, Nb) blocks per
     query block, and differs from the float64 selection only for blocks whose
     proxy lies within the band of the row's k-th largest proxy."""
-    q, k, _ = inp.head64(b, h)
+    q, k, _ = _head(inp, b, h, order)
     keep, p, pk = orc.route_topk(q, k, inp.wl.block, topk, scale)
     gm = gpu_mask.astype(bool)
     nb = keep.shape[0]
@@ -86,19 +101,24 @@ def mask_check_topk(inp, b, h, gpu_mask: np.ndarray, topk: int, scale=None):
 
 
 def output_check(inp, b, h, o_gpu: torch.Tensor, lse_gpu: torch.Tensor, keep: np.ndarray, tau: float,
-                 correction: bool, qblocks=None, scale=None, dense=False):
-    """Oracle output for the given query blocks of head (b, h) against the GPU's."""
+                 correction: bool, qblocks=None, scale=None, dense=False, order=None):
+    """Oracle output for the given query blocks of head (b, h) against the GPU's.
+
+    order: position -> token map (3-D tile order); qblocks and keep then index
+    blocks of positions, and the rows compared are the tokens they hold."""
     wl = inp.wl
     q, k, v = inp.head64(b, h)
     N = q.shape[0]
     ranges = orc.block_ranges(N, wl.block)
     qblocks = list(range(len(ranges))) if qblocks is None else sorted(set(qblocks))
     rows = np.concatenate([np.arange(*ranges[I]) for I in qblocks])
+    if order is not None:
+        rows = np.asarray(order)[rows]
     if dense:
         o_ref, lse_ref = orc.dense_head(q, k, v, scale, rows=rows)
     else:
         o_full, lse_full, _ = orc.forward_head(q, k, v, wl.block, tau, correction, scale, keep=keep,
-                                               qblocks=qblocks)
+                                               qblocks=qblocks, order=order)
         o_ref, lse_ref = o_full[rows], lse_full[rows]
     o = o_gpu[b, h].float().cpu().numpy().astype(np.float64)[rows]
     lse = lse_gpu[b, h].cpu().numpy().astype(np.float64)[rows]

@@ -35,7 +35,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_abi_version(lib):
-    assert api.sa_abi_version() == 2
+    assert api.sa_abi_version() == 3
 
 
 def test_status_strings(lib):
@@ -52,8 +52,8 @@ def _inputs(qk=api.SA_BF16, v=api.SA_BF16, q=FAKE, k=FAKE, vv=FAKE, qs=None, ks=
     return api.Inputs(q, k, vv, qs, ks, qk, v)
 
 
-def _params(block=64, tau=2.0, corr=1, scale=0.0, topk=0):
-    return api.Params(block, tau, corr, scale, topk)
+def _params(block=64, tau=2.0, corr=1, scale=0.0, topk=0, tile=(0, 0, 0)):
+    return api.Params(block, tau, corr, scale, topk, *tile)
 
 
 def _fwd(lib, sh, pr, inp, o=FAKE, lse=FAKE, kept=None, ws=FAKE, ws_bytes=1 << 40):
@@ -98,6 +98,9 @@ def test_bad_shapes(lib, kw, code):
     (dict(scale=math.inf), "SA_ERR_PARAM"),
     (dict(topk=-1), "SA_ERR_PARAM"),
     (dict(topk=-5, tau=math.nan), "SA_ERR_PARAM"),
+    (dict(tile=(4, 4, 2)), "SA_ERR_PARAM"),        # volume 32
+    (dict(tile=(0, 8, 8)), "SA_ERR_PARAM"),        # partly zero
+    (dict(tile=(-1, -8, 8)), "SA_ERR_PARAM"),
 ])
 def test_bad_params(lib, kw, code):
     assert api.status_name(_fwd(lib, _shape(), _params(**kw), _inputs())) == code
@@ -157,9 +160,27 @@ def test_empty_calls_are_ok_without_pointers(lib, kw):
 
 
 def test_params_struct_layout():
-    # sa_params in include/sa_route.h: block, tau, correction, scale, topk
-    assert ctypes.sizeof(api.Params) == 20
-    assert [f[0] for f in api.Params._fields_] == ["block", "tau", "correction", "scale", "topk"]
+    # sa_params in include/sa_route.h: block, tau, correction, scale, topk, tile_t/h/w
+    assert ctypes.sizeof(api.Params) == 32
+    assert [f[0] for f in api.Params._fields_] == ["block", "tau", "correction", "scale", "topk",
+                                                    "tile_t", "tile_h", "tile_w"]
+
+
+def test_tile_order_with_fp8_is_unsupported(lib):
+    inp = _inputs(qk=api.SA_FP8_E4M3, v=api.SA_BF16, qs=FAKE, ks=FAKE)
+    st = _fwd(lib, _shape(), _params(tile=(4, 4, 4)), inp)
+    assert api.status_name(st) == "SA_ERR_UNSUPPORTED"
+
+
+def test_tiled_workspace_holds_k_in_tile_order(lib):
+    sh = _shape(B=1, H=3, T=1, Hg=10, Wg=13, D=128)     # N = 130
+    n0 = lib.sa_workspace_bytes(ctypes.byref(sh), ctypes.byref(_params()), ctypes.byref(_inputs()))
+    n1 = lib.sa_workspace_bytes(ctypes.byref(sh), ctypes.byref(_params(tile=(1, 8, 8))), ctypes.byref(_inputs()))
+    assert n1 - n0 == (3 * 130 * 128 * 2 + 255) // 256 * 256
+    # fp32 reads K through the order directly: no copy
+    f32 = _inputs(api.SA_F32, api.SA_F32)
+    assert lib.sa_workspace_bytes(ctypes.byref(sh), ctypes.byref(_params(tile=(1, 8, 8))), ctypes.byref(f32)) == \
+        lib.sa_workspace_bytes(ctypes.byref(sh), ctypes.byref(_params()), ctypes.byref(f32))
 
 
 @pytest.mark.parametrize("sparsity,N,expect", [
@@ -177,3 +198,15 @@ def test_budget_blocks(sparsity, N, expect):
 def test_budget_blocks_rejects_out_of_range(sparsity):
     with pytest.raises(ValueError):
         api.budget_blocks(sparsity, 640)
+
+
+def test_last_status_explains_a_zero_size(lib):
+    sh = _shape()
+    inp = _inputs(qk=api.SA_FP8_E4M3, v=api.SA_BF16)
+    n = lib.sa_workspace_bytes(ctypes.byref(sh), ctypes.byref(_params(tile=(4, 4, 4))), ctypes.byref(inp))
+    assert n == 0 and api.status_name(lib.sa_last_status()) == "SA_ERR_UNSUPPORTED"
+    n = lib.sa_workspace_bytes(ctypes.byref(sh), ctypes.byref(_params()), ctypes.byref(_inputs()))
+    assert n > 0 and lib.sa_last_status() == 0
+    bad = _shape(D=96)
+    assert lib.sa_dense_workspace_bytes(ctypes.byref(bad), ctypes.byref(_inputs())) == 0
+    assert api.status_name(lib.sa_last_status()) == "SA_ERR_SHAPE"
