@@ -15,7 +15,9 @@ library launches on, around each launch inside the timed region.  The
 cpu_baseline leg times the float64 CPU oracle on a bounded sample of the same
 workload (a few query blocks of one head) and reports it in the same unit.
 The fixed_budget list times the same call with routing by a fixed number of
-key blocks per query block (sparsity 0.9 and 0.8 by default) instead of tau.
+key blocks per query block (sparsity 0.9 and 0.8 by default) instead of tau;
+the tile_order list times it with blocks formed over 3-D tiles of the token
+grid (4x4x4 and 1x8x8 by default).
 """
 from __future__ import annotations
 
@@ -141,6 +143,8 @@ def main() -> None:
     ap.add_argument("--budgets", default="0.9,0.8",
                     help="fixed-budget routing sparsities to time as well (comma list, '' for none)")
     ap.add_argument("--budget-steps", type=int, default=5)
+    ap.add_argument("--tiles", default="4x4x4,1x8x8",
+                    help="3-D tile orders (t x h x w, product 64) to time at the same tau ('' for none)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run one 1 GiB device-to-device copy (reference for the PMC byte counters)")
     args = ap.parse_args()
@@ -284,6 +288,46 @@ def main() -> None:
                         "speedup_vs_dense": (dense["ms"] / bms) if dense else None})
         log(f"budget sparsity {sp}: topk {topk}, {bms:.2f} ms")
 
+    # 3-D tile token order (blocks are tiles of the token grid) at the same tau
+    tiled = []
+    for spec in [x for x in args.tiles.split(",") if x.strip()]:
+        tile = tuple(int(t) for t in spec.lower().split("x"))
+        if wl.dtype == "fp8":
+            break                       # fp8 block scales belong to raster blocks
+        wst = torch.empty(api.sa_workspace_bytes(q, k, v, grid, tile=tile), dtype=torch.uint8, device=dev)
+        tmask, tkept = api.sa_route(q, k, v, grid, tau=tau, tile=tile, workspace=wst)
+        torch.cuda.synchronize()
+        tmask_np = tmask.cpu().numpy().reshape(wl.B * wl.H, wl.Nb, wl.Nb)
+        del tmask
+        tf = computed_block_flops(tmask_np, wl.N, wl.D)
+
+        def tstep(ev=None):
+            if ev is not None:
+                ev[0].record()
+            api.sa_pool(q, k, v, grid, tau=tau, correction=correction, workspace=wst, tile=tile)
+            if ev is not None:
+                ev[1].record()
+            api.sa_forward_pooled(q, k, v, grid, tau=tau, correction=correction, workspace=wst, tile=tile,
+                                  out=ob, lse=lseb, kept=kept, want_kept=True)
+            if ev is not None:
+                ev[2].record()
+        tstep()
+        torch.cuda.synchronize()
+        assert torch.equal(kept.cpu(), tkept.cpu()), "fused routing disagrees with sa_route (tiles)"
+        tevs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.budget_steps)]
+        for i in range(args.budget_steps):
+            tstep(tevs[i])
+        torch.cuda.synchronize()
+        tpool = float(np.mean([e[0].elapsed_time(e[1]) for e in tevs]))
+        tms = float(np.mean([e[0].elapsed_time(e[2]) for e in tevs]))
+        tiled.append({"tile": list(tile), "tau": tau, "ms": tms, "pool_ms": tpool,
+                      "computed_block_tflops": tf / (tms * 1e-3) / 1e12,
+                      "block_density": float(tmask_np.mean()),
+                      "union_inflation": union_inflation(tmask_np),
+                      "speedup_vs_dense": (dense["ms"] / tms) if dense else None})
+        log(f"tile {spec}: density {tmask_np.mean():.3f}, {tms:.2f} ms")
+        del wst
+
     if args.calibrate_copy:
         src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)
@@ -333,6 +377,7 @@ def main() -> None:
                      "achieved_incl_correction": (f_exact + f_corr) / (fused_avg * 1e-3) / 1e12},
         "dense": dense,
         "fixed_budget": budgets,
+        "tile_order": tiled,
         "cpu_baseline": cpu,
         "kernel_src": kernel_source_hash(),
     }
