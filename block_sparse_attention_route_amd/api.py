@@ -56,6 +56,10 @@ class Params(ctypes.Structure):
                 ("tile_t", ctypes.c_int32), ("tile_h", ctypes.c_int32), ("tile_w", ctypes.c_int32)]
 
 
+class Prologue(ctypes.Structure):
+    _fields_ = [("norm_eps", ctypes.c_float), ("rope_base", ctypes.c_float)]
+
+
 class Inputs(ctypes.Structure):
     _fields_ = [("q", ctypes.c_void_p), ("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
                 ("q_scale", ctypes.c_void_p), ("k_scale", ctypes.c_void_p),
@@ -96,6 +100,8 @@ def load_library():
     for fn in (lib.sa_forward, lib.sa_forward_pooled):
         fn.restype = st
         fn.argtypes = [P, S, I, vp, vp, vp, vp, sz, vp]
+    lib.sa_qk_prologue.restype = st
+    lib.sa_qk_prologue.argtypes = [P, S, ctypes.POINTER(Prologue), I, vp, vp, vp, vp, vp, sz, vp]
     lib.sa_dense_forward.restype = st
     lib.sa_dense_forward.argtypes = [P, ctypes.c_float, I, vp, vp, vp, sz, vp]
     _lib = lib
@@ -249,6 +255,26 @@ def sa_forward_pooled(q, k, v, grid, *, tau: float = math.inf, correction: bool 
     _check(lib.sa_forward_pooled(ctypes.byref(sh), ctypes.byref(pr), ctypes.byref(inp), _ptr(out), _ptr(lse),
                                  _ptr(kept), _ptr(workspace), workspace.numel(), _stream(q)))
     return out, lse, kept
+
+
+def sa_qk_prologue(xq, xk, v, grid, q_gain, k_gain, *, norm_eps: float = 1e-6, rope_base: float = 10000.0,
+                   tau: float = math.inf, topk: int = 0, tile=None, workspace=None, q_out=None, k_out=None):
+    """Fused producer step: RMS norm + gain + 3-D rotary embedding of the raw
+    Q/K projections (bf16) into q_out / k_out, with the pool's workspace
+    filled from them.  Returns (q_out, k_out, workspace); follow with
+    sa_forward_pooled(q_out, k_out, v, ...) using the same tau/topk/tile."""
+    lib = load_library()
+    ws = _workspace(sa_workspace_bytes(xq, xk, v, grid, tile=tile), xq, workspace)
+    if q_out is None:
+        q_out = torch.empty_like(xq)
+    if k_out is None:
+        k_out = torch.empty_like(xk)
+    sh, pr, inp = make_shape(xq, grid), make_params(tau, True, 0.0, topk, tile), make_inputs(xq, xk, v)
+    pro = Prologue(float(norm_eps), float(rope_base))
+    _check(lib.sa_qk_prologue(ctypes.byref(sh), ctypes.byref(pr), ctypes.byref(pro), ctypes.byref(inp),
+                              _ptr(q_gain), _ptr(k_gain), _ptr(q_out), _ptr(k_out), _ptr(ws), ws.numel(),
+                              _stream(xq)))
+    return q_out, k_out, ws
 
 
 def sa_dense_forward(q, k, v, grid, *, scale: float = 0.0, workspace=None, q_scale=None, k_scale=None,

@@ -338,6 +338,38 @@ SA_API sa_status sa_forward(const sa_shape* shape, const sa_params* params, cons
   return run_attn(r, in, o, lse, kept, ws, true, st);
 }
 
+SA_API sa_status sa_qk_prologue(const sa_shape* shape, const sa_params* params, const sa_prologue* pro,
+                                const sa_inputs* in, const float* q_gain, const float* k_gain, void* q_out,
+                                void* k_out, void* ws, size_t ws_bytes, void* stream) {
+  Req r{};
+  sa_status s;
+  if ((s = check_shape_inputs(shape, in, &r, false)) != SA_OK) return s;
+  if ((s = check_params(params, &r)) != SA_OK) return s;
+  if (!pro) return fail(SA_ERR_NULL, "prologue params are NULL");
+  if (!(pro->norm_eps > 0.f) || !std::isfinite(pro->norm_eps))
+    return fail(SA_ERR_PARAM, "norm_eps must be positive and finite");
+  if (!(pro->rope_base > 0.f) || !std::isfinite(pro->rope_base))
+    return fail(SA_ERR_PARAM, "rope_base must be positive and finite");
+  if (r.qk != SA_BF16) return fail(SA_ERR_UNSUPPORTED, "the producer step takes bf16 Q/K/V");
+  if (r.empty) return ok();
+  if (!q_gain || !k_gain || !q_out || !k_out) return fail(SA_ERR_NULL, "gain or output is NULL");
+  if (!aligned(q_gain, 4) || !aligned(k_gain, 4)) return fail(SA_ERR_ALIGN, "gains must be 4-byte aligned");
+  if (!aligned(q_out, 16) || !aligned(k_out, 16)) return fail(SA_ERR_ALIGN, "outputs must be 16-byte aligned");
+  if ((s = check_ws(ws, ws_bytes, r)) != SA_OK) return s;
+  sa::PoolArgs a = pool_args(r, in, ws, false);
+  a.pro.on = true;
+  a.pro.q_gain = q_gain;
+  a.pro.k_gain = k_gain;
+  a.pro.q_out = static_cast<uint16_t*>(q_out);
+  a.pro.k_out = static_cast<uint16_t*>(k_out);
+  a.pro.eps = pro->norm_eps;
+  a.pro.base = pro->rope_base;
+  a.pro.T = r.T;
+  a.pro.Hg = r.Hg;
+  a.pro.Wg = r.Wg;
+  return hip_status(sa::launch_pool(a, (hipStream_t)stream), "producer kernel launch");
+}
+
 SA_API sa_status sa_dense_forward(const sa_shape* shape, float scale, const sa_inputs* in, void* o,
                                   float* lse, void* ws, size_t ws_bytes, void* stream) {
   Req r{};

@@ -6,9 +6,18 @@
 // this library reads "pooled" as the mean over each 64-token block's actual
 // tokens.  Blocks are taken over positions: the raster order, or the 3-D
 // tile order of the token grid (sa_layout.h, token_of), in which case K is
-// also written out in position order.  The kernel is HBM-bound: it reads Q, K and V once (each workgroup
-// one 64-token block of one head, all three tensors in flight together) and
-// writes 1/16 as many bytes of means plus the regrouped V.
+// also written out in position order.  The kernel is HBM-bound: it reads Q, K
+// and V once (each workgroup one 64-token block of one head, all three
+// tensors in flight together) and writes 1/16 as many bytes of means plus
+// the regrouped V.
+//
+// With the producer step fused in front (ProArgs), the rows read are the raw
+// Q/K projections: each is RMS-normalised over its D features, scaled by the
+// gain, rotated pairwise by its 3-D position (frame, row and column groups of
+// feature pairs), rounded to bf16, written to q_out / k_out, and pooled from
+// the rounded values -- the same bits sa_pool would read back.  The paper
+// review of the Sol Video Inference Engine (xllm-io blog) lists fused
+// RoPE + norm and fused QK + RoPE among the fusions in front of attention.
 //
 // Every sum is taken in one fixed order (per-thread sequential over rows,
 // then the partial sums of the row groups in order), so the means, and all
@@ -109,6 +118,69 @@ __device__ __forceinline__ void block_mean(const u32x4 (&raw)[Tiling<E, D>::P], 
   __syncthreads();
 }
 
+// RMS norm + gain + 3-D rotary embedding of this thread's rows, in place on
+// the raw bf16 chunks, rounded to bf16; the rows are stored to `out` (token
+// order).  Thread (c, g) owns features 8c .. 8c+7 = feature pairs 4c .. 4c+3
+// of rows g, g+G, ...; the CPR threads of a row are adjacent lanes.
+template <int D, int NP>
+__device__ __forceinline__ void norm_rope_rows(u32x4 (&raw)[NP], int pos0, int nrows, const TileMap& tm,
+                                               const float* __restrict__ gain, const ProArgs& pr,
+                                               uint16_t* __restrict__ out) {
+  using T = Tiling<ELT_BF16, D>;
+  static_assert(NP == T::P, "rows per thread");
+  const int c = threadIdx.x % T::CPR, g = threadIdx.x / T::CPR;
+  // rotary groups: D - 4*(D/6) features for the frame, 2*(D/6) each for rows, columns
+  constexpr int DY = 2 * (D / 6), DT = D - 2 * DY;
+  float theta[4];
+  int axis[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int f = 8 * c + 2 * q;  // first feature of the pair
+    int j, da;
+    if (f < DT) {
+      axis[q] = 0; j = f / 2; da = DT;
+    } else if (f < DT + DY) {
+      axis[q] = 1; j = (f - DT) / 2; da = DY;
+    } else {
+      axis[q] = 2; j = (f - DT - DY) / 2; da = DY;
+    }
+    theta[q] = powf(pr.base, -2.0f * (float)j / (float)da);
+  }
+  float gv[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) gv[e] = gain[8 * c + e];
+#pragma unroll
+  for (int i = 0; i < T::P; ++i) {
+    const int r = g + T::G * i;
+    const bool valid = r < nrows;
+    float x[8];
+    unpack<ELT_BF16>(raw[i], x);
+    float ss = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) ss = fmaf(x[e], x[e], ss);
+#pragma unroll
+    for (int off = 1; off < T::CPR; off <<= 1) ss += __shfl_xor(ss, off);
+    if (!valid) continue;
+    const float inv = 1.0f / sqrtf(ss / (float)D + pr.eps);
+    const int tok = token_of(tm, pos0 + r);
+    const int pt = tok / (pr.Hg * pr.Wg), py = (tok / pr.Wg) % pr.Hg, px = tok % pr.Wg;
+    u32x4 w;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const float pa = (float)(axis[q] == 0 ? pt : (axis[q] == 1 ? py : px));
+      float sn, cs;
+      sincosf(pa * theta[q], &sn, &cs);
+      const float u = x[2 * q] * inv * gv[2 * q];
+      const float v = x[2 * q + 1] * inv * gv[2 * q + 1];
+      const uint32_t lo = f32_to_bf16_bits(u * cs - v * sn);
+      const uint32_t hi = f32_to_bf16_bits(u * sn + v * cs);
+      w[q] = lo | (hi << 16);
+    }
+    raw[i] = w;
+    *reinterpret_cast<u32x4*>(out + (size_t)tok * D + 8 * c) = w;
+  }
+}
+
 template <int QE, int VE, int D, bool VT_ONLY>
 __global__ __launch_bounds__(256) void pool_kernel(PoolArgs a) {
   const int J = blockIdx.x;
@@ -129,6 +201,12 @@ __global__ __launch_bounds__(256) void pool_kernel(PoolArgs a) {
     load_block<QE, D>(reinterpret_cast<const uint8_t*>(a.k) + head0 * D * TQ::B, row0, nrows, tm, rk);
   }
   load_block<VE, D>(reinterpret_cast<const uint8_t*>(a.v) + head0 * D * TV::B, row0, nrows, tm, rv);
+  if constexpr (!VT_ONLY && QE == ELT_BF16) {
+    if (a.pro.on) {
+      norm_rope_rows<D>(rq, row0, nrows, tm, a.pro.q_gain, a.pro, a.pro.q_out + head0 * D);
+      norm_rope_rows<D>(rk, row0, nrows, tm, a.pro.k_gain, a.pro, a.pro.k_out + head0 * D);
+    }
+  }
 
   if constexpr (!VT_ONLY && QE == ELT_BF16) {
     // 3-D tile order: K also in position order, for the attention kernel's

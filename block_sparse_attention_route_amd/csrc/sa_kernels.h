@@ -11,6 +11,19 @@ namespace sa {
 
 enum Elt : int { ELT_F32 = 0, ELT_BF16 = 1, ELT_FP8 = 2 };
 
+// Fused Q/K producer in front of the pool (per-head RMS norm with gain,
+// 3-D rotary embedding, bf16 rounding): the transformed rows are written to
+// q_out / k_out and pooled in place of the inputs.
+struct ProArgs {
+  bool on;
+  const float* q_gain;   // [D]
+  const float* k_gain;   // [D]
+  uint16_t* q_out;       // [BH][N][D] bf16, token order
+  uint16_t* k_out;
+  float eps, base;
+  int T, Hg, Wg;
+};
+
 struct PoolArgs {
   const void* q;
   const void* k;
@@ -28,6 +41,7 @@ struct PoolArgs {
   uint16_t* vt16;
   TileMap tm;            // position -> token order (on == 0: raster)
   uint16_t* kpos16;      // K in position order, written when tm.on (bf16 K)
+  ProArgs pro;           // producer step fused in front (pro.on)
 };
 
 struct RouteArgs {

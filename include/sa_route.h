@@ -130,6 +130,12 @@ typedef struct sa_inputs {
   int32_t v_dtype;
 } sa_inputs;
 
+/* Parameters of the fused Q/K producer step (sa_qk_prologue). */
+typedef struct sa_prologue {
+  float norm_eps;   /* RMS-norm epsilon, > 0 */
+  float rope_base;  /* rotary frequency base, > 0 (10000 in most models) */
+} sa_prologue;
+
 /* ABI version of the loaded library (SA_ABI_VERSION it was built with). */
 int32_t sa_abi_version(void);
 
@@ -179,6 +185,29 @@ sa_status sa_forward(const sa_shape* shape, const sa_params* params, const sa_in
 sa_status sa_forward_pooled(const sa_shape* shape, const sa_params* params, const sa_inputs* in,
                             void* o, float* lse, int32_t* kept, void* ws, size_t ws_bytes,
                             void* stream);
+
+/* Fused Q/K producer step in place of sa_pool (the paper review of the Sol
+ * Video Inference Engine, xllm-io blog, lists fused RoPE + norm and fused
+ * QK + RoPE among the fusions in front of attention).  in->q and in->k hold
+ * the raw per-head Q/K projections [B, H, N, D] (bf16), in->v the values
+ * (bf16).  Every token row of Q and of K is
+ *   RMS-normalised over its D features: x / sqrt(mean(x^2) + norm_eps),
+ *   scaled by the gain (q_gain / k_gain: [D] fp32, shared by the heads),
+ *   rotated pairwise by its grid position: feature pairs (2j, 2j+1) form
+ *   three consecutive groups -- D - 4*(D/6) features for the frame index t,
+ *   2*(D/6) for the row y, 2*(D/6) for the column x -- and pair j of a group
+ *   of d_a features turns by pos_a * rope_base^(-2j/d_a) radians,
+ *   rounded to bf16 and written to q_out / k_out ([B, H, N, D] bf16, token
+ *   order; they may be in->q / in->k themselves, in place).
+ * The workspace then holds exactly what sa_pool would compute from q_out,
+ * k_out and v (block means over the blocks that params selects, the bf16
+ * copies, V regrouped, K in tile order), so sa_forward_pooled with inputs
+ * {q_out, k_out, v} completes the attention.  params is used for its block
+ * order and workspace layout only.  Only bf16 Q/K/V (SA_ERR_UNSUPPORTED
+ * otherwise); gains 4-byte aligned, outputs 16-byte aligned. */
+sa_status sa_qk_prologue(const sa_shape* shape, const sa_params* params, const sa_prologue* pro,
+                         const sa_inputs* in, const float* q_gain, const float* k_gain, void* q_out,
+                         void* k_out, void* ws, size_t ws_bytes, void* stream);
 
 /* Workspace bytes for sa_dense_forward (0 on invalid arguments). */
 size_t sa_dense_workspace_bytes(const sa_shape* shape, const sa_inputs* in);

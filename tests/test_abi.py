@@ -210,3 +210,30 @@ def test_last_status_explains_a_zero_size(lib):
     bad = _shape(D=96)
     assert lib.sa_dense_workspace_bytes(ctypes.byref(bad), ctypes.byref(_inputs())) == 0
     assert api.status_name(lib.sa_last_status()) == "SA_ERR_SHAPE"
+
+
+def _pro(lib, eps=1e-6, base=1e4, inp=None, gq=FAKE, gk=FAKE, qo=FAKE, ko=FAKE):
+    sh, pr = _shape(), _params()
+    inp = _inputs() if inp is None else inp
+    p = api.Prologue(eps, base)
+    return lib.sa_qk_prologue(ctypes.byref(sh), ctypes.byref(pr), ctypes.byref(p), ctypes.byref(inp),
+                              gq, gk, qo, ko, FAKE, 1 << 40, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(eps=0.0), "SA_ERR_PARAM"),
+    (dict(eps=math.nan), "SA_ERR_PARAM"),
+    (dict(base=-1.0), "SA_ERR_PARAM"),
+    (dict(base=math.inf), "SA_ERR_PARAM"),
+    (dict(gq=None), "SA_ERR_NULL"),
+    (dict(ko=None), "SA_ERR_NULL"),
+    (dict(qo=FAKE + 4), "SA_ERR_ALIGN"),
+    (dict(gk=FAKE + 2), "SA_ERR_ALIGN"),
+])
+def test_prologue_validation(lib, kw, code):
+    assert api.status_name(_pro(lib, **kw)) == code
+
+
+def test_prologue_needs_bf16(lib):
+    st = _pro(lib, inp=_inputs(api.SA_F32, api.SA_F32))
+    assert api.status_name(st) == "SA_ERR_UNSUPPORTED"
