@@ -17,7 +17,8 @@ workload (a few query blocks of one head) and reports it in the same unit.
 The fixed_budget list times the same call with routing by a fixed number of
 key blocks per query block (sparsity 0.9 and 0.8 by default) instead of tau;
 the tile_order list times it with blocks formed over 3-D tiles of the token
-grid (4x4x4 and 1x8x8 by default).
+grid (4x4x4 and 1x8x8 by default); fused_producer times sa_qk_prologue (norm
++ rotary + pool of the Q/K projections) in place of the pool.
 """
 from __future__ import annotations
 
@@ -288,6 +289,29 @@ def main() -> None:
                         "speedup_vs_dense": (dense["ms"] / bms) if dense else None})
         log(f"budget sparsity {sp}: topk {topk}, {bms:.2f} ms")
 
+    # fused Q/K producer step (norm + rotary + pool) in place of the pool: the
+    # workload's Q/K stand in for the raw projections
+    producer = None
+    if wl.dtype == "bf16":
+        gq = torch.ones(wl.D, dtype=torch.float32, device=dev)
+        qo, ko = torch.empty_like(q), torch.empty_like(k)
+        wsp = torch.empty_like(ws)
+        api.sa_qk_prologue(q, k, v, grid, gq, gq, tau=tau, workspace=wsp, q_out=qo, k_out=ko)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(args.budget_steps):
+            api.sa_qk_prologue(q, k, v, grid, gq, gq, tau=tau, workspace=wsp, q_out=qo, k_out=ko)
+        e1.record()
+        torch.cuda.synchronize()
+        pms = e0.elapsed_time(e1) / args.budget_steps
+        pbytes = pool_bytes + 2 * wl.B * wl.H * wl.N * wl.D * 2       # + Q and K written back
+        producer = {"ms": pms, "gbs": pbytes / (pms * 1e-3) / 1e9,
+                    "frac_hbm": pbytes / (pms * 1e-3) / 1e9 / PEAK_HBM_GBS, "bytes": pbytes,
+                    "unfused_extra_bytes": 2 * wl.B * wl.H * wl.N * wl.D * 2}
+        log(f"fused producer: {pms:.3f} ms")
+        del qo, ko, wsp
+
     # 3-D tile token order (blocks are tiles of the token grid) at the same tau
     tiled = []
     for spec in [x for x in args.tiles.split(",") if x.strip()]:
@@ -378,6 +402,7 @@ def main() -> None:
         "dense": dense,
         "fixed_budget": budgets,
         "tile_order": tiled,
+        "fused_producer": producer,
         "cpu_baseline": cpu,
         "kernel_src": kernel_source_hash(),
     }

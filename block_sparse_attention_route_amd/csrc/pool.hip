@@ -118,14 +118,14 @@ __device__ __forceinline__ void block_mean(const u32x4 (&raw)[Tiling<E, D>::P], 
   __syncthreads();
 }
 
-// RMS norm + gain + 3-D rotary embedding of this thread's rows, in place on
-// the raw bf16 chunks, rounded to bf16; the rows are stored to `out` (token
-// order).  Thread (c, g) owns features 8c .. 8c+7 = feature pairs 4c .. 4c+3
-// of rows g, g+G, ...; the CPR threads of a row are adjacent lanes.
+// RMS norm + gain + 3-D rotary embedding of this thread's Q and K rows, in
+// place on the raw bf16 chunks, rounded to bf16; the rows are stored to
+// q_out / k_out (token order).  Thread (c, g) owns features 8c .. 8c+7 =
+// feature pairs 4c .. 4c+3 of rows g, g+G, ...; the CPR threads of a row are
+// adjacent lanes.  Q and K of a token share its rotation angles.
 template <int D, int NP>
-__device__ __forceinline__ void norm_rope_rows(u32x4 (&raw)[NP], int pos0, int nrows, const TileMap& tm,
-                                               const float* __restrict__ gain, const ProArgs& pr,
-                                               uint16_t* __restrict__ out) {
+__device__ __forceinline__ void norm_rope_qk(u32x4 (&rq)[NP], u32x4 (&rk)[NP], int pos0, int nrows,
+                                             const TileMap& tm, const ProArgs& pr, size_t head0) {
   using T = Tiling<ELT_BF16, D>;
   static_assert(NP == T::P, "rows per thread");
   const int c = threadIdx.x % T::CPR, g = threadIdx.x / T::CPR;
@@ -146,38 +146,50 @@ __device__ __forceinline__ void norm_rope_rows(u32x4 (&raw)[NP], int pos0, int n
     }
     theta[q] = powf(pr.base, -2.0f * (float)j / (float)da);
   }
-  float gv[8];
+  float gq[8], gk[8];
 #pragma unroll
-  for (int e = 0; e < 8; ++e) gv[e] = gain[8 * c + e];
+  for (int e = 0; e < 8; ++e) {
+    gq[e] = pr.q_gain[8 * c + e];
+    gk[e] = pr.k_gain[8 * c + e];
+  }
 #pragma unroll
   for (int i = 0; i < T::P; ++i) {
     const int r = g + T::G * i;
-    const bool valid = r < nrows;
-    float x[8];
-    unpack<ELT_BF16>(raw[i], x);
-    float ss = 0.f;
+    float xq[8], xk[8];
+    unpack<ELT_BF16>(rq[i], xq);
+    unpack<ELT_BF16>(rk[i], xk);
+    float sq = 0.f, sk = 0.f;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) ss = fmaf(x[e], x[e], ss);
+    for (int e = 0; e < 8; ++e) {
+      sq = fmaf(xq[e], xq[e], sq);
+      sk = fmaf(xk[e], xk[e], sk);
+    }
 #pragma unroll
-    for (int off = 1; off < T::CPR; off <<= 1) ss += __shfl_xor(ss, off);
-    if (!valid) continue;
-    const float inv = 1.0f / sqrtf(ss / (float)D + pr.eps);
+    for (int off = 1; off < T::CPR; off <<= 1) {
+      sq += __shfl_xor(sq, off);
+      sk += __shfl_xor(sk, off);
+    }
+    if (r >= nrows) continue;
+    const float iq = 1.0f / sqrtf(sq / (float)D + pr.eps);
+    const float ik = 1.0f / sqrtf(sk / (float)D + pr.eps);
     const int tok = token_of(tm, pos0 + r);
     const int pt = tok / (pr.Hg * pr.Wg), py = (tok / pr.Wg) % pr.Hg, px = tok % pr.Wg;
-    u32x4 w;
+    u32x4 wq, wk;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const float pa = (float)(axis[q] == 0 ? pt : (axis[q] == 1 ? py : px));
       float sn, cs;
       sincosf(pa * theta[q], &sn, &cs);
-      const float u = x[2 * q] * inv * gv[2 * q];
-      const float v = x[2 * q + 1] * inv * gv[2 * q + 1];
-      const uint32_t lo = f32_to_bf16_bits(u * cs - v * sn);
-      const uint32_t hi = f32_to_bf16_bits(u * sn + v * cs);
-      w[q] = lo | (hi << 16);
+      const float uq = xq[2 * q] * iq * gq[2 * q], vq = xq[2 * q + 1] * iq * gq[2 * q + 1];
+      const float uk = xk[2 * q] * ik * gk[2 * q], vk = xk[2 * q + 1] * ik * gk[2 * q + 1];
+      wq[q] = (uint32_t)f32_to_bf16_bits(uq * cs - vq * sn) | ((uint32_t)f32_to_bf16_bits(uq * sn + vq * cs) << 16);
+      wk[q] = (uint32_t)f32_to_bf16_bits(uk * cs - vk * sn) | ((uint32_t)f32_to_bf16_bits(uk * sn + vk * cs) << 16);
     }
-    raw[i] = w;
-    *reinterpret_cast<u32x4*>(out + (size_t)tok * D + 8 * c) = w;
+    rq[i] = wq;
+    rk[i] = wk;
+    const size_t at = (head0 + (size_t)tok) * D + 8 * c;
+    *reinterpret_cast<u32x4*>(pr.q_out + at) = wq;
+    *reinterpret_cast<u32x4*>(pr.k_out + at) = wk;
   }
 }
 
@@ -202,10 +214,7 @@ __global__ __launch_bounds__(256) void pool_kernel(PoolArgs a) {
   }
   load_block<VE, D>(reinterpret_cast<const uint8_t*>(a.v) + head0 * D * TV::B, row0, nrows, tm, rv);
   if constexpr (!VT_ONLY && QE == ELT_BF16) {
-    if (a.pro.on) {
-      norm_rope_rows<D>(rq, row0, nrows, tm, a.pro.q_gain, a.pro, a.pro.q_out + head0 * D);
-      norm_rope_rows<D>(rk, row0, nrows, tm, a.pro.k_gain, a.pro, a.pro.k_out + head0 * D);
-    }
+    if (a.pro.on) norm_rope_qk<D>(rq, rk, row0, nrows, tm, a.pro, head0);
   }
 
   if constexpr (!VT_ONLY && QE == ELT_BF16) {
