@@ -85,15 +85,11 @@ __device__ __forceinline__ void load_block(const uint8_t* __restrict__ head, int
   }
 }
 
-// mean over rows -> out[0..D) (fp32), scaled by mult; uses part[G][D] in LDS.
+// Per-thread sums over its rows (sequential, rows g, g+G, ...; absent rows
+// hold zeros) -> acc.
 template <int E, int D>
-__device__ __forceinline__ void block_mean(const u32x4 (&raw)[Tiling<E, D>::P], int nrows,
-                                           float mult, float* __restrict__ part,
-                                           float* __restrict__ out_f32,
-                                           uint16_t* __restrict__ out_bf16) {
+__device__ __forceinline__ void thread_sums(const u32x4 (&raw)[Tiling<E, D>::P], float (&acc)[Tiling<E, D>::EPC]) {
   using T = Tiling<E, D>;
-  const int c = threadIdx.x % T::CPR, g = threadIdx.x / T::CPR;
-  float acc[T::EPC];
 #pragma unroll
   for (int e = 0; e < T::EPC; ++e) acc[e] = 0.f;
 #pragma unroll
@@ -103,6 +99,16 @@ __device__ __forceinline__ void block_mean(const u32x4 (&raw)[Tiling<E, D>::P], 
 #pragma unroll
     for (int e = 0; e < T::EPC; ++e) acc[e] += x[e];
   }
+}
+
+// Per-thread sums -> mean over rows in out[0..D) (fp32), scaled by mult; the
+// row groups' partial sums are added in order through part[G][D] in LDS.
+template <int E, int D>
+__device__ __forceinline__ void mean_finish(const float (&acc)[Tiling<E, D>::EPC], int nrows, float mult,
+                                            float* __restrict__ part, float* __restrict__ out_f32,
+                                            uint16_t* __restrict__ out_bf16) {
+  using T = Tiling<E, D>;
+  const int c = threadIdx.x % T::CPR, g = threadIdx.x / T::CPR;
 #pragma unroll
   for (int e = 0; e < T::EPC; ++e) part[g * D + c * T::EPC + e] = acc[e];
   __syncthreads();
@@ -118,18 +124,36 @@ __device__ __forceinline__ void block_mean(const u32x4 (&raw)[Tiling<E, D>::P], 
   __syncthreads();
 }
 
-// RMS norm + gain + 3-D rotary embedding of this thread's Q and K rows, in
-// place on the raw bf16 chunks, rounded to bf16; the rows are stored to
-// q_out / k_out (token order).  Thread (c, g) owns features 8c .. 8c+7 =
-// feature pairs 4c .. 4c+3 of rows g, g+G, ...; the CPR threads of a row are
-// adjacent lanes.  Q and K of a token share its rotation angles.
+// mean over rows -> out[0..D) (fp32), scaled by mult; uses part[G][D] in LDS.
+template <int E, int D>
+__device__ __forceinline__ void block_mean(const u32x4 (&raw)[Tiling<E, D>::P], int nrows,
+                                           float mult, float* __restrict__ part,
+                                           float* __restrict__ out_f32,
+                                           uint16_t* __restrict__ out_bf16) {
+  float acc[Tiling<E, D>::EPC];
+  thread_sums<E, D>(raw, acc);
+  mean_finish<E, D>(acc, nrows, mult, part, out_f32, out_bf16);
+}
+
+// Rotation angles of this thread's rows: (cos, sin) of pos_a * theta for its
+// four feature pairs, pairs split into consecutive frame / row / column
+// groups of D - 4*(D/6), 2*(D/6), 2*(D/6) features and pair j of a group of
+// d_a features turning at theta = base^(-2 j / d_a).  Thread (c, g) owns
+// features 8c .. 8c+7 = pairs 4c .. 4c+3 of rows g, g+G, ...  The angles of
+// a position are the same for every head, so a workgroup computes them once
+// for all the heads it produces.
 template <int D, int NP>
-__device__ __forceinline__ void norm_rope_qk(u32x4 (&rq)[NP], u32x4 (&rk)[NP], int pos0, int nrows,
-                                             const TileMap& tm, const ProArgs& pr, size_t head0) {
+struct RopeRows {
+  float cs[NP][4], sn[NP][4];
+  int tok[NP];
+};
+
+template <int D, int NP>
+__device__ __forceinline__ void rope_rows(int pos0, int nrows, const TileMap& tm, const ProArgs& pr,
+                                          RopeRows<D, NP>& out) {
   using T = Tiling<ELT_BF16, D>;
   static_assert(NP == T::P, "rows per thread");
   const int c = threadIdx.x % T::CPR, g = threadIdx.x / T::CPR;
-  // rotary groups: D - 4*(D/6) features for the frame, 2*(D/6) each for rows, columns
   constexpr int DY = 2 * (D / 6), DT = D - 2 * DY;
   float theta[4];
   int axis[4];
@@ -146,64 +170,72 @@ __device__ __forceinline__ void norm_rope_qk(u32x4 (&rq)[NP], u32x4 (&rk)[NP], i
     }
     theta[q] = powf(pr.base, -2.0f * (float)j / (float)da);
   }
-  float gq[8], gk[8];
 #pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    gq[e] = pr.q_gain[8 * c + e];
-    gk[e] = pr.k_gain[8 * c + e];
-  }
-#pragma unroll
-  for (int i = 0; i < T::P; ++i) {
+  for (int i = 0; i < NP; ++i) {
     const int r = g + T::G * i;
-    float xq[8], xk[8];
-    unpack<ELT_BF16>(rq[i], xq);
-    unpack<ELT_BF16>(rk[i], xk);
-    float sq = 0.f, sk = 0.f;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      sq = fmaf(xq[e], xq[e], sq);
-      sk = fmaf(xk[e], xk[e], sk);
-    }
-#pragma unroll
-    for (int off = 1; off < T::CPR; off <<= 1) {
-      sq += __shfl_xor(sq, off);
-      sk += __shfl_xor(sk, off);
-    }
-    if (r >= nrows) continue;
-    const float iq = 1.0f / sqrtf(sq / (float)D + pr.eps);
-    const float ik = 1.0f / sqrtf(sk / (float)D + pr.eps);
-    const int tok = token_of(tm, pos0 + r);
+    const int tok = token_of(tm, pos0 + (r < nrows ? r : 0));
+    out.tok[i] = tok;
     const int pt = tok / (pr.Hg * pr.Wg), py = (tok / pr.Wg) % pr.Hg, px = tok % pr.Wg;
-    u32x4 wq, wk;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const float pa = (float)(axis[q] == 0 ? pt : (axis[q] == 1 ? py : px));
-      float sn, cs;
-      sincosf(pa * theta[q], &sn, &cs);
-      const float uq = xq[2 * q] * iq * gq[2 * q], vq = xq[2 * q + 1] * iq * gq[2 * q + 1];
-      const float uk = xk[2 * q] * ik * gk[2 * q], vk = xk[2 * q + 1] * ik * gk[2 * q + 1];
-      wq[q] = (uint32_t)f32_to_bf16_bits(uq * cs - vq * sn) | ((uint32_t)f32_to_bf16_bits(uq * sn + vq * cs) << 16);
-      wk[q] = (uint32_t)f32_to_bf16_bits(uk * cs - vk * sn) | ((uint32_t)f32_to_bf16_bits(uk * sn + vk * cs) << 16);
+      sincosf(pa * theta[q], &out.sn[i][q], &out.cs[i][q]);
     }
-    rq[i] = wq;
-    rk[i] = wk;
-    const size_t at = (head0 + (size_t)tok) * D + 8 * c;
-    *reinterpret_cast<u32x4*>(pr.q_out + at) = wq;
-    *reinterpret_cast<u32x4*>(pr.k_out + at) = wk;
   }
 }
 
-template <int QE, int VE, int D, bool VT_ONLY>
-__global__ __launch_bounds__(256) void pool_kernel(PoolArgs a) {
-  const int J = blockIdx.x;
-  const int bh = blockIdx.y;
+// RMS norm + gain + rotation of this thread's rows of one tensor (Q or K),
+// in place on the raw bf16 chunks, rounded to bf16; the rows are stored to
+// out (token order) and their sums over the thread's rows returned in acc.  The CPR threads of a row are
+// adjacent lanes.
+template <int D, int NP>
+__device__ __forceinline__ void norm_rope(u32x4 (&raw)[NP], int nrows, const float* __restrict__ gain,
+                                          float eps, const RopeRows<D, NP>& ang, uint16_t* __restrict__ out,
+                                          float (&acc)[8]) {
+  using T = Tiling<ELT_BF16, D>;
+  const int c = threadIdx.x % T::CPR, g = threadIdx.x / T::CPR;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+  float gv[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) gv[e] = gain[8 * c + e];
+#pragma unroll
+  for (int i = 0; i < NP; ++i) {
+    const int r = g + T::G * i;
+    float x[8];
+    unpack<ELT_BF16>(raw[i], x);
+    float ss = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) ss = fmaf(x[e], x[e], ss);
+#pragma unroll
+    for (int off = 1; off < T::CPR; off <<= 1) ss += __shfl_xor(ss, off);
+    if (r >= nrows) continue;
+    const float inv = 1.0f / sqrtf(ss / (float)D + eps);
+    u32x4 w;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const float cs = ang.cs[i][q], sn = ang.sn[i][q];
+      const float u = x[2 * q] * inv * gv[2 * q], v = x[2 * q + 1] * inv * gv[2 * q + 1];
+      w[q] = (uint32_t)f32_to_bf16_bits(u * cs - v * sn) | ((uint32_t)f32_to_bf16_bits(u * sn + v * cs) << 16);
+    }
+    raw[i] = w;
+    *reinterpret_cast<u32x4*>(out + (size_t)ang.tok[i] * D + 8 * c) = w;
+    // the block sums of the rounded values, in the order thread_sums takes
+    // (absent rows would add +0, which leaves a sum started at +0 unchanged)
+    float y[8];
+    unpack<ELT_BF16>(w, y);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] += y[e];
+  }
+}
+
+// One 64-token block J of head bh: load, (producer step), means, V regrouped.
+template <int QE, int VE, int D, bool VT_ONLY, bool PRO>
+__device__ __forceinline__ void pool_block(const PoolArgs& a, int J, int bh, float* part, uint16_t* vtl,
+                                           const RopeRows<D, Tiling<ELT_BF16, D>::P>* ang) {
   const int row0 = J * kBlock;
   const int nrows = min(kBlock, a.N - row0);
   const size_t head0 = (size_t)bh * a.N;
-
-  __shared__ float part[4096];  // up to 64 row groups x 64 dims or 32 x 128
-  __shared__ __attribute__((aligned(16))) uint16_t vtl[D * kBlock];
-
   using TQ = Tiling<QE, D>;
   using TV = Tiling<VE, D>;
   u32x4 rq[TQ::P], rk[TQ::P], rv[TV::P];
@@ -213,82 +245,131 @@ __global__ __launch_bounds__(256) void pool_kernel(PoolArgs a) {
     load_block<QE, D>(reinterpret_cast<const uint8_t*>(a.k) + head0 * D * TQ::B, row0, nrows, tm, rk);
   }
   load_block<VE, D>(reinterpret_cast<const uint8_t*>(a.v) + head0 * D * TV::B, row0, nrows, tm, rv);
-  if constexpr (!VT_ONLY && QE == ELT_BF16) {
-    if (a.pro.on) norm_rope_qk<D>(rq, rk, row0, nrows, tm, a.pro, head0);
-  }
-
-  if constexpr (!VT_ONLY && QE == ELT_BF16) {
-    // 3-D tile order: K also in position order, for the attention kernel's
-    // contiguous tile copies
-    if (tm.on) {
-      const int c = threadIdx.x % TQ::CPR, g = threadIdx.x / TQ::CPR;
-      uint8_t* dst = reinterpret_cast<uint8_t*>(a.kpos16) + (head0 + row0) * D * 2;
-#pragma unroll
-      for (int i = 0; i < TQ::P; ++i) {
-        const int r = g + TQ::G * i;
-        if (r < nrows) *reinterpret_cast<u32x4*>(dst + (size_t)r * D * 2 + c * 16) = rk[i];
-      }
-    }
-  }
-
   const size_t mrow = ((size_t)bh * a.Nb + J) * D;
-  if constexpr (!VT_ONLY) {
-    float qm = 1.f, km = 1.f;
-    if constexpr (QE == ELT_FP8) {
-      qm = a.q_scale[(size_t)bh * a.Nb + J];
-      km = a.k_scale[(size_t)bh * a.Nb + J];
-    }
-    block_mean<QE, D>(rq, nrows, qm, part, a.qbar + mrow, nullptr);
-    uint16_t* k16 = (VE == ELT_BF16) ? a.kbar16 + ((size_t)bh * a.Nbp + J) * D : nullptr;
-    block_mean<QE, D>(rk, nrows, km, part, a.kbar + mrow, k16);
-    block_mean<VE, D>(rv, nrows, 1.f, part, a.vbar + mrow, nullptr);
-  }
 
-  if constexpr (VE == ELT_BF16) {
-    // V^T of this block into LDS: element (d, r) at row d, 16-byte chunk
-    // (r/8) ^ ((d/8) & 7), slot r % 8 (rows are 64 keys = 128 bytes).
-    const int c = threadIdx.x % TV::CPR, g = threadIdx.x / TV::CPR;
-#pragma unroll
-    for (int i = 0; i < TV::P; ++i) {
-      const int r = g + TV::G * i;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int d = c * 8 + e;
-        const uint32_t word = rv[i][e >> 1];
-        const uint16_t val = (e & 1) ? (uint16_t)(word >> 16) : (uint16_t)(word & 0xFFFFu);
-        const int pc = (r >> 3) ^ ((d >> 3) & 7);
-        vtl[d * kBlock + pc * 8 + (r & 7)] = val;
-      }
-    }
-    __syncthreads();
-    uint8_t* dst = reinterpret_cast<uint8_t*>(a.vt16 + ((size_t)bh * a.Nb + J) * D * kBlock);
-    constexpr int NCH = D * kBlock * 2 / 16;  // 16-byte chunks in the tile
-#pragma unroll
-    for (int x = threadIdx.x; x < NCH; x += 256) {
-      const int d = x >> 3, cc = x & 7;
-      const int pc = cc ^ ((d >> 3) & 7);
-      *reinterpret_cast<u32x4*>(dst + (size_t)x * 16) =
-          *reinterpret_cast<const u32x4*>(&vtl[d * kBlock + pc * 8]);
-    }
+  auto qk_part = [&]() {
     if constexpr (!VT_ONLY) {
-      // bf16(vbar) into the transposed groups of 64 blocks.
-      if (threadIdx.x < D) {
-        const int d = threadIdx.x;
-        const size_t grp = (size_t)bh * (a.Nbp / 64) + (J >> 6);
-        a.vbarT16[(grp * D + d) * 64 + (J & 63)] = f32_to_bf16_bits(a.vbar[mrow + d]);
+      if constexpr (PRO) {
+        // the producer writes Q/K in token order; the means come from the
+        // rounded values
+        static_assert(QE == ELT_BF16, "producer step on bf16 rows");
+        float acc[8];
+        norm_rope<D>(rq, nrows, a.pro.q_gain, a.pro.eps, *ang, a.pro.q_out + head0 * D, acc);
+        mean_finish<QE, D>(acc, nrows, 1.f, part, a.qbar + mrow, nullptr);
+        norm_rope<D>(rk, nrows, a.pro.k_gain, a.pro.eps, *ang, a.pro.k_out + head0 * D, acc);
+        mean_finish<QE, D>(acc, nrows, 1.f, part, a.kbar + mrow, a.kbar16 + ((size_t)bh * a.Nbp + J) * D);
+        if (tm.on) {
+          // 3-D tile order: K also in position order
+          const int c = threadIdx.x % TQ::CPR, g = threadIdx.x / TQ::CPR;
+          uint8_t* dst = reinterpret_cast<uint8_t*>(a.kpos16) + (head0 + row0) * D * 2;
+#pragma unroll
+          for (int i = 0; i < TQ::P; ++i) {
+            const int r = g + TQ::G * i;
+            if (r < nrows)
+              *reinterpret_cast<u32x4*>(dst + (size_t)r * D * 2 + c * 16) = rk[i];
+          }
+        }
+        return;
       }
-      // the last block of a head zero-fills the padding up to Nbp
-      if (J == a.Nb - 1) {
-        for (int JJ = a.Nb; JJ < a.Nbp; ++JJ) {
-          if (threadIdx.x < D) {
-            const int d = threadIdx.x;
-            a.kbar16[((size_t)bh * a.Nbp + JJ) * D + d] = 0;
-            const size_t grp = (size_t)bh * (a.Nbp / 64) + (JJ >> 6);
-            a.vbarT16[(grp * D + d) * 64 + (JJ & 63)] = 0;
+      if constexpr (QE == ELT_BF16) {
+        // 3-D tile order: K also in position order, for the attention
+        // kernel's contiguous tile copies
+        if (tm.on) {
+          const int c = threadIdx.x % TQ::CPR, g = threadIdx.x / TQ::CPR;
+          uint8_t* dst = reinterpret_cast<uint8_t*>(a.kpos16) + (head0 + row0) * D * 2;
+#pragma unroll
+          for (int i = 0; i < TQ::P; ++i) {
+            const int r = g + TQ::G * i;
+            if (r < nrows) *reinterpret_cast<u32x4*>(dst + (size_t)r * D * 2 + c * 16) = rk[i];
           }
         }
       }
+      float qm = 1.f, km = 1.f;
+      if constexpr (QE == ELT_FP8) {
+        qm = a.q_scale[(size_t)bh * a.Nb + J];
+        km = a.k_scale[(size_t)bh * a.Nb + J];
+      }
+      block_mean<QE, D>(rq, nrows, qm, part, a.qbar + mrow, nullptr);
+      uint16_t* k16 = (VE == ELT_BF16) ? a.kbar16 + ((size_t)bh * a.Nbp + J) * D : nullptr;
+      block_mean<QE, D>(rk, nrows, km, part, a.kbar + mrow, k16);
     }
+  };
+
+  auto v_part = [&]() {
+    if constexpr (!VT_ONLY) block_mean<VE, D>(rv, nrows, 1.f, part, a.vbar + mrow, nullptr);
+    if constexpr (VE == ELT_BF16) {
+      // V^T of this block into LDS: element (d, r) at row d, 16-byte chunk
+      // (r/8) ^ ((d/8) & 7), slot r % 8 (rows are 64 keys = 128 bytes).
+      const int c = threadIdx.x % TV::CPR, g = threadIdx.x / TV::CPR;
+#pragma unroll
+      for (int i = 0; i < TV::P; ++i) {
+        const int r = g + TV::G * i;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int d = c * 8 + e;
+          const uint32_t word = rv[i][e >> 1];
+          const uint16_t val = (e & 1) ? (uint16_t)(word >> 16) : (uint16_t)(word & 0xFFFFu);
+          const int pc = (r >> 3) ^ ((d >> 3) & 7);
+          vtl[d * kBlock + pc * 8 + (r & 7)] = val;
+        }
+      }
+      __syncthreads();
+      uint8_t* dst = reinterpret_cast<uint8_t*>(a.vt16 + ((size_t)bh * a.Nb + J) * D * kBlock);
+      constexpr int NCH = D * kBlock * 2 / 16;  // 16-byte chunks in the tile
+#pragma unroll
+      for (int x = threadIdx.x; x < NCH; x += 256) {
+        const int d = x >> 3, cc = x & 7;
+        const int pc = cc ^ ((d >> 3) & 7);
+        *reinterpret_cast<u32x4*>(dst + (size_t)x * 16) =
+            *reinterpret_cast<const u32x4*>(&vtl[d * kBlock + pc * 8]);
+      }
+      if constexpr (!VT_ONLY) {
+        // bf16(vbar) into the transposed groups of 64 blocks.
+        if (threadIdx.x < D) {
+          const int d = threadIdx.x;
+          const size_t grp = (size_t)bh * (a.Nbp / 64) + (J >> 6);
+          a.vbarT16[(grp * D + d) * 64 + (J & 63)] = f32_to_bf16_bits(a.vbar[mrow + d]);
+        }
+        // the last block of a head zero-fills the padding up to Nbp
+        if (J == a.Nb - 1) {
+          for (int JJ = a.Nb; JJ < a.Nbp; ++JJ) {
+            if (threadIdx.x < D) {
+              const int d = threadIdx.x;
+              a.kbar16[((size_t)bh * a.Nbp + JJ) * D + d] = 0;
+              const size_t grp = (size_t)bh * (a.Nbp / 64) + (JJ >> 6);
+              a.vbarT16[(grp * D + d) * 64 + (JJ & 63)] = 0;
+            }
+          }
+        }
+      }
+      // vtl is rewritten by the next head's block
+      __syncthreads();
+    }
+  };
+
+  qk_part();
+  v_part();
+}
+
+#ifndef SA_PRO_HEADS
+#define SA_PRO_HEADS 8
+#endif
+// heads per workgroup of the producer step (they share the rotation angles)
+constexpr int kProHeads = SA_PRO_HEADS;
+
+template <int QE, int VE, int D, bool VT_ONLY, bool PRO>
+__global__ __launch_bounds__(256) void pool_kernel(PoolArgs a) {
+  __shared__ float part[4096];  // up to 64 row groups x 64 dims or 32 x 128
+  __shared__ __attribute__((aligned(16))) uint16_t vtl[D * kBlock];
+  const int J = blockIdx.x;
+  if constexpr (PRO) {
+    RopeRows<D, Tiling<ELT_BF16, D>::P> ang;
+    rope_rows<D>(J * kBlock, min(kBlock, a.N - J * kBlock), a.tm, a.pro, ang);
+    const int bh0 = blockIdx.y * kProHeads;
+    const int bh1 = min(bh0 + kProHeads, a.BH);
+    for (int bh = bh0; bh < bh1; ++bh) pool_block<QE, VE, D, VT_ONLY, true>(a, J, bh, part, vtl, &ang);
+  } else {
+    pool_block<QE, VE, D, VT_ONLY, false>(a, J, blockIdx.y, part, vtl, nullptr);
   }
 }
 
@@ -297,12 +378,19 @@ hipError_t launch_t(const PoolArgs& a, hipStream_t st) {
   dim3 grid(a.Nb, a.BH);
   if (a.vt_only) {
     if constexpr (VE == ELT_BF16) {
-      hipLaunchKernelGGL((pool_kernel<QE, VE, D, true>), grid, dim3(256), 0, st, a);
+      hipLaunchKernelGGL((pool_kernel<QE, VE, D, true, false>), grid, dim3(256), 0, st, a);
     } else {
       return hipSuccess;
     }
+  } else if (a.pro.on) {
+    if constexpr (QE == ELT_BF16) {
+      const dim3 pgrid(a.Nb, (a.BH + kProHeads - 1) / kProHeads);
+      hipLaunchKernelGGL((pool_kernel<QE, VE, D, false, true>), pgrid, dim3(256), 0, st, a);
+    } else {
+      return hipErrorInvalidValue;
+    }
   } else {
-    hipLaunchKernelGGL((pool_kernel<QE, VE, D, false>), grid, dim3(256), 0, st, a);
+    hipLaunchKernelGGL((pool_kernel<QE, VE, D, false, false>), grid, dim3(256), 0, st, a);
   }
   return hipGetLastError();
 }
