@@ -200,7 +200,7 @@ __global__ __launch_bounds__(128 * QB, QB == 2 ? 2 : 1) void attn_kernel(AttnArg
   const int N = a.N, Nb = a.Nb;
   const int ngroups = (Nb + QB - 1) / QB;
   const int G = a.BH * ngroups;
-  const int tile = xcd_remap((int)blockIdx.x, G);
+  const int tile = xcd_remap<SPARSE ? SA_XCD_CHUNK_SPARSE : SA_XCD_CHUNK>((int)blockIdx.x, G);
   const int bh = tile / ngroups;
   const int grp = tile - bh * ngroups;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;

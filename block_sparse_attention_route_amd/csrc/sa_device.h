@@ -340,17 +340,24 @@ __device__ __forceinline__ void topk_rows(const float* __restrict__ p, int Nb, i
 #ifndef SA_XCD_CHUNK
 #define SA_XCD_CHUNK 64
 #endif
+#ifndef SA_XCD_CHUNK_SPARSE
+#define SA_XCD_CHUNK_SPARSE 16
+#endif
 
 // XCD-aware tile order.  Workgroups are handed to the 8 XCDs round-robin, so
 // workgroup w runs on XCD w % 8 as that XCD's (w / 8)-th workgroup.  Tiles
-// are cut into chunks of SA_XCD_CHUNK consecutive tiles (adjacent query
-// blocks of one head, about as many as an XCD holds at once) and chunk c goes
-// to XCD c % 8: the workgroups resident on one XCD share key blocks in its
-// L2, and all eight XCDs stay on the same head at a time, so the head's K/V
-// stays resident in the shared last-level cache.  SA_XCD_CHUNK = 0 keeps the
-// plain order.  Tiles past the last whole round keep their own index.
+// are cut into chunks of CH consecutive tiles (adjacent query blocks of one
+// head) and chunk c goes to XCD c % 8: the workgroups resident on one XCD
+// share key blocks in its L2, and all eight XCDs stay on the same head at a
+// time, so the head's K/V stays resident in the shared last-level cache.
+// Dense workgroups all cost the same and take chunks of about what an XCD
+// holds at once (SA_XCD_CHUNK); sparse ones differ in cost with the kept
+// density of their region, and smaller chunks (SA_XCD_CHUNK_SPARSE) spread
+// each region over the XCDs, which have no work stealing between them.
+// CH = 0 keeps the plain order.  Tiles past the last whole round keep their
+// own index.
+template <int CH>
 __device__ __forceinline__ int xcd_remap(int w, int G) {
-  constexpr int CH = SA_XCD_CHUNK;
   if constexpr (CH == 0) {
     return w;
   } else {
