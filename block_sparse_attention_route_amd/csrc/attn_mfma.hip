@@ -135,6 +135,22 @@ __device__ __forceinline__ void dma16(const void* gsrc, uint32_t lds_wave_base) 
                : "memory", "m0");
 }
 
+// The same copy from a wave-uniform base address (scalar registers) plus a
+// per-lane 32-bit byte offset, so a tile's copies need no per-lane address
+// arithmetic once the offsets are known.
+__device__ __forceinline__ uint64_t uniform_addr(const void* p) {
+  const uint64_t u = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)u);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(u >> 32));
+  return ((uint64_t)hi << 32) | lo;
+}
+__device__ __forceinline__ void dma16s(uint32_t voff, uint64_t sbase, uint32_t lds_wave_base) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
+               :
+               : "v"(voff), "s"(sbase), "s"(__builtin_amdgcn_readfirstlane(lds_wave_base))
+               : "memory", "m0");
+}
+
 // One float from a wave-uniform global address through the scalar unit,
 // waited for inside the same statement: a vector load here would make the
 // compiler wait for the in-flight tile copies as well.
@@ -282,6 +298,23 @@ __global__ __launch_bounds__(128 * QB, QB == 2 ? 2 : 1) void attn_kernel(AttnArg
     return it;
   };
 
+  // Per-lane source offsets of the copies of a full tile (the same for the K
+  // rows of an exact tile and the kbar rows of a correction tile, and for
+  // both kinds of V^T tile).
+  uint32_t koff[KI16], voff[VI];
+#pragma unroll
+  for (int i = 0; i < KI16; ++i) {
+    const int P = (wave + NW * i) * 1024 + 16 * lane;
+    const int row = P / C::KROW16, pc = (P % C::KROW16) / 16;
+    koff[i] = row * C::KROW16 + swz<C::CPR16>(row, pc) * 16;
+  }
+#pragma unroll
+  for (int i = 0; i < VI; ++i) {
+    const int P = (wave + NW * i) * 1024 + 16 * lane;
+    const int row = P / 128, pc = (P % 128) / 16;
+    voff[i] = row * 128 + swz<8>(row, pc) * 16;
+  }
+
   // Issue the LDS-DMA copies of tile `it` into stage `stg`.  Wave w's i-th
   // copy fills LDS bytes [(w + NW*i) KiB, +1 KiB) of the K or V^T buffer; lane
   // l writes 16 bytes at +16*l, i.e. physical chunk pc of row r, which holds
@@ -296,7 +329,7 @@ __global__ __launch_bounds__(128 * QB, QB == 2 ? 2 : 1) void attn_kernel(AttnArg
       ksrc = reinterpret_cast<const uint8_t*>(a.kbar16 + ((size_t)bh * a.Nbp + 64 * it) * D);
       vsrc = reinterpret_cast<const uint8_t*>(a.vbarT16 + ((size_t)bh * (a.Nbp / 64) + it) * D * 64);
     } else {
-      const int J = tile_block(it);
+      const int J = __builtin_amdgcn_readfirstlane(tile_block(it));
       k8 = FP8;
       // keys in position order: the caller's K, or its copy in tile order
       const void* kpos = (!FP8 && a.tm.on) ? static_cast<const void*>(a.kpos16) : a.k;
@@ -306,6 +339,14 @@ __global__ __launch_bounds__(128 * QB, QB == 2 ? 2 : 1) void attn_kernel(AttnArg
     }
     const uint32_t kb = smem_base + stg * C::STAGE;
     const uint32_t vb = kb + C::KTILE;
+    if (!k8 && kvalid == kBlock) {
+      const uint64_t kbase = uniform_addr(ksrc), vbase = uniform_addr(vsrc);
+#pragma unroll
+      for (int i = 0; i < KI16; ++i) dma16s(koff[i], kbase, kb + (wave + NW * i) * 1024);
+#pragma unroll
+      for (int i = 0; i < VI; ++i) dma16s(voff[i], vbase, vb + (wave + NW * i) * 1024);
+      return;
+    }
     if (k8) {
 #pragma unroll
       for (int i = 0; i < KI8; ++i) {
@@ -349,12 +390,15 @@ __global__ __launch_bounds__(128 * QB, QB == 2 ? 2 : 1) void attn_kernel(AttnArg
   // One tile: publish it, prefetch the tile ST-1 ahead, then S^T, softmax
   // and PV.  KIND selects the masks at compile time, so the plain exact
   // tiles -- nearly all of them -- carry no per-key selects.
-  auto step = [&](int it, auto kindc) __attribute__((always_inline)) {
+  // STG >= 0: the ring stage of tile `it`, known at compile time (then the
+  // LDS operand addresses are immediate offsets); -1: it % ST.
+  auto step = [&](int it, auto kindc, auto stgc) __attribute__((always_inline)) {
     constexpr int KIND = decltype(kindc)::value;
-    const int stg = it % ST;
+    constexpr int STG = decltype(stgc)::value;
+    const int stg = STG >= 0 ? STG : it % ST;
     wait_tiles_ahead<LPT, ST - 2>(min(ST - 2, ntiles - 1 - it));
     __syncthreads();
-    if (it + ST - 1 < ntiles) issue_tile(it + ST - 1, (it + ST - 1) % ST);
+    if (it + ST - 1 < ntiles) issue_tile(it + ST - 1, STG >= 0 ? (STG + ST - 1) % ST : (it + ST - 1) % ST);
 
     constexpr bool virt = KIND == kVirt;
     int J = 0;
@@ -441,15 +485,26 @@ __global__ __launch_bounds__(128 * QB, QB == 2 ? 2 : 1) void attn_kernel(AttnArg
     }
 
     // ---- online softmax (row = this lane's query; keys split with lane^32).
-    // The maximum in use is raised only when a row's maximum exceeds it by
-    // more than 2^kLazy: exact, since numerator and denominator share it.
-    float mt = s[0][0];
+    bf16x8 pb[4];
+    float rs = 0.f;
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    const bf16x2 ones = {static_cast<__bf16>(1.f), static_cast<__bf16>(1.f)};
+    // bf16 weights 2^(s*c2 - m) of this lane's 32 keys and their sum
+    auto weights = [&](float negm) __attribute__((always_inline)) {
+      rs = 0.f;
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
+      for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) mt = fmaxf(mt, s[kt][r]);
-    mt = xor32_max(mt) * c2;
-    if (__builtin_expect(__any(mt > m_run + kLazy), 0)) {
+        for (int r = 0; r < 16; r += 2) {
+          const __bf16 b0 = static_cast<__bf16>(__builtin_amdgcn_exp2f(fmaf(s[kt][r], c2, negm)));
+          const __bf16 b1 = static_cast<__bf16>(__builtin_amdgcn_exp2f(fmaf(s[kt][r + 1], c2, negm)));
+          pb[2 * kt + (r >> 3)][r & 7] = b0;
+          pb[2 * kt + (r >> 3)][(r & 7) + 1] = b1;
+          const bf16x2 pair = {b0, b1};
+          rs = __builtin_amdgcn_fdot2_f32_bf16(pair, ones, rs, false);
+        }
+    };
+    auto raise_max = [&](float mt) __attribute__((always_inline)) {
       const float mn = fmaxf(m_run, mt);
       const float alpha = (mn == kNegInf) ? 1.f : __builtin_amdgcn_exp2f(m_run - mn);
       m_run = mn;
@@ -458,23 +513,22 @@ __global__ __launch_bounds__(128 * QB, QB == 2 ? 2 : 1) void attn_kernel(AttnArg
       for (int dt = 0; dt < C::DT; ++dt)
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[dt][r] *= alpha;
+    };
+    auto tile_max = [&]() __attribute__((always_inline)) {
+      float mt = s[0][0];
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mt = fmaxf(mt, s[kt][r]);
+      return xor32_max(mt) * c2;
+    };
+    // The maximum in use is raised only when a row's maximum exceeds it by
+    // more than 2^kLazy: exact, since numerator and denominator share it.
+    {
+      const float mt = tile_max();
+      if (__builtin_expect(__any(mt > m_run + kLazy), 0)) raise_max(mt);
     }
-    const float negm = (m_run == kNegInf) ? 0.f : -m_run;
-    bf16x8 pb[4];
-    float rs = 0.f;
-    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-    const bf16x2 ones = {static_cast<__bf16>(1.f), static_cast<__bf16>(1.f)};
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-      for (int r = 0; r < 16; r += 2) {
-        const __bf16 b0 = static_cast<__bf16>(__builtin_amdgcn_exp2f(fmaf(s[kt][r], c2, negm)));
-        const __bf16 b1 = static_cast<__bf16>(__builtin_amdgcn_exp2f(fmaf(s[kt][r + 1], c2, negm)));
-        pb[2 * kt + (r >> 3)][r & 7] = b0;
-        pb[2 * kt + (r >> 3)][(r & 7) + 1] = b1;
-        const bf16x2 pair = {b0, b1};
-        rs = __builtin_amdgcn_fdot2_f32_bf16(pair, ones, rs, false);
-      }
+    weights((m_run == kNegInf) ? 0.f : -m_run);
     l_run += rs;
 
     // ---- O^T += V^T P^T
@@ -491,9 +545,24 @@ __global__ __launch_bounds__(128 * QB, QB == 2 ? 2 : 1) void attn_kernel(AttnArg
   // virtual (correction) tiles first, then the exact tiles of the union list
   // in key order, the ragged last key block -- always last -- on its own
   const bool has_tail = ntiles > nvirt && ntail < kBlock && tile_block(ntiles - 1) == Nb - 1;
-  for (int it = 0; it < nvirt; ++it) step(it, std::integral_constant<int, kVirt>{});
-  for (int it = nvirt; it < ntiles - (has_tail ? 1 : 0); ++it) step(it, std::integral_constant<int, kPlain>{});
-  if (has_tail) step(ntiles - 1, std::integral_constant<int, kTail>{});
+  // tiles [it0, it1) of one kind; with a two-stage ring in pairs, so that
+  // each copy of the body knows its stage
+  auto run = [&](int it0, int it1, auto kindc) __attribute__((always_inline)) {
+    if constexpr (ST == 2) {
+      int it = it0;
+      if (it < it1 && (it & 1)) step(it++, kindc, std::integral_constant<int, 1>{});
+      for (; it + 1 < it1; it += 2) {
+        step(it, kindc, std::integral_constant<int, 0>{});
+        step(it + 1, kindc, std::integral_constant<int, 1>{});
+      }
+      if (it < it1) step(it, kindc, std::integral_constant<int, 0>{});
+    } else {
+      for (int it = it0; it < it1; ++it) step(it, kindc, std::integral_constant<int, -1>{});
+    }
+  };
+  run(0, nvirt, std::integral_constant<int, kVirt>{});
+  run(nvirt, ntiles - (has_tail ? 1 : 0), std::integral_constant<int, kPlain>{});
+  if (has_tail) step(ntiles - 1, std::integral_constant<int, kTail>{}, std::integral_constant<int, -1>{});
 
   // --------------------------------------------------------------- 4. epilogue
   const float lt = l_run + __shfl_xor(l_run, 32);
