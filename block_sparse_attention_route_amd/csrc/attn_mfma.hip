@@ -42,11 +42,15 @@
 // the same head (shared key blocks hit in that XCD's L2, the head's K/V stays
 // in the last-level cache).
 //
-// Softmax.  The running maximum is raised lazily: only when a row's new
-// maximum exceeds the one in use by more than 2^8 are l and the accumulators
-// rescaled.  This is exact -- numerator and denominator carry the same stale
-// maximum, and P <= 2^8 stays well inside bf16 -- and makes the rescale rare.
-// Row sums are taken over the bf16-rounded P that enters the PV product.
+// Softmax.  The running maximum is raised lazily and without a per-tile
+// maximum: the weights P = 2^(s - m) are taken against the maximum in use,
+// and only when some row's weights of a tile exceed 2^64 (or overflow) are
+// the row maxima taken, l and the accumulators rescaled and the tile's
+// weights redone.  This is exact -- numerator and denominator carry the same
+// stale maximum, and weights up to 2^64 keep their relative precision in
+// bf16 and fp32 -- and makes the rescale rare (in practice a row's first
+// tile).  Row sums are taken over the bf16-rounded P that enters the PV
+// product.
 #include <type_traits>
 
 #include "sa_device.h"
@@ -55,7 +59,10 @@
 namespace sa {
 namespace {
 
-constexpr float kLazy = 8.0f;  // log2 headroom of the lazily raised running maximum
+// The running maximum is raised lazily: weights are taken against it as it
+// stands, and only a tile whose weights exceed kWeightMax (2^64) raises it.
+constexpr float kWeightMax = 18446744073709551616.0f;
+constexpr float kMInit = -1e30f;  // finite start of the running maximum
 
 // Kinds of key tile: block means (correction), a full exact block, the
 // ragged last exact block.
@@ -378,7 +385,7 @@ __global__ __launch_bounds__(128 * QB, QB == 2 ? 2 : 1) void attn_kernel(AttnArg
   for (int dt = 0; dt < C::DT; ++dt)
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[dt][r] = 0.f;
-  float m_run = kNegInf, l_run = 0.f;
+  float m_run = kMInit, l_run = 0.f;
 
   const float c2_base = a.scale * kLog2e;  // logits in log2 units
   const float log2_tail = log2f((float)ntail);
@@ -522,13 +529,18 @@ __global__ __launch_bounds__(128 * QB, QB == 2 ? 2 : 1) void attn_kernel(AttnArg
         for (int r = 0; r < 16; ++r) mt = fmaxf(mt, s[kt][r]);
       return xor32_max(mt) * c2;
     };
-    // The maximum in use is raised only when a row's maximum exceeds it by
-    // more than 2^kLazy: exact, since numerator and denominator share it.
-    {
-      const float mt = tile_max();
-      if (__builtin_expect(__any(mt > m_run + kLazy), 0)) raise_max(mt);
+    // No per-tile maximum: the weights are taken against the maximum in use
+    // as it stands, and only a tile in which some row's weights exceed 2^64
+    // or are not finite -- its maximum lies more than 64 above the one in use
+    // (log2 units), as on a row's first tile, where the maximum in use is
+    // kMInit -- raises it and is redone.  Exact: numerator and denominator
+    // share the maximum, and weights up to 2^64 keep their relative precision
+    // in bf16 and in the fp32 sums (masked keys give 2^-inf = 0).
+    weights(-m_run);
+    if (__builtin_expect(__any(!(rs <= kWeightMax)), 0)) {
+      raise_max(tile_max());
+      weights(-m_run);
     }
-    weights((m_run == kNegInf) ? 0.f : -m_run);
     l_run += rs;
 
     // ---- O^T += V^T P^T
