@@ -100,31 +100,40 @@ __device__ __forceinline__ void proxy_rows(const float* __restrict__ qbar,
   for (int r = 0; r < QB; ++r)
 #pragma unroll
     for (int e = 0; e < DPL; ++e) qv[r][e] = (r < nrows) ? qbar[r * D + sub * DPL + e] : 0.f;
-  for (int J0 = 0; J0 < Nb; J0 += ROWS_PER_PASS) {
-    const int J = J0 + slot;
-    float acc[QB];
+  // U passes at a time, their loads issued together (the key means come
+  // from L2 or beyond; one pass at a time would wait out that latency U times)
+  constexpr int U = 4;
+  for (int J0 = 0; J0 < Nb; J0 += ROWS_PER_PASS * U) {
+    f32x4 kv[U][DPL / 4];
 #pragma unroll
-    for (int r = 0; r < QB; ++r) acc[r] = 0.f;
-    if (J < Nb) {
-      const f32x4* row = reinterpret_cast<const f32x4*>(kbar + (size_t)J * D + sub * DPL);
+    for (int u = 0; u < U; ++u) {
+      const int J = J0 + u * ROWS_PER_PASS + slot;
+      const f32x4* row = reinterpret_cast<const f32x4*>(kbar + (size_t)(J < Nb ? J : 0) * D + sub * DPL);
 #pragma unroll
-      for (int e4 = 0; e4 < DPL / 4; ++e4) {
-        const f32x4 kv = row[e4];
+      for (int e4 = 0; e4 < DPL / 4; ++e4) kv[u][e4] = row[e4];
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int J = J0 + u * ROWS_PER_PASS + slot;
+      float acc[QB];
+#pragma unroll
+      for (int r = 0; r < QB; ++r) acc[r] = 0.f;
+#pragma unroll
+      for (int e4 = 0; e4 < DPL / 4; ++e4)
 #pragma unroll
         for (int e = 0; e < 4; ++e)
 #pragma unroll
-          for (int r = 0; r < QB; ++r) acc[r] = fmaf(qv[r][e4 * 4 + e], kv[e], acc[r]);
+          for (int r = 0; r < QB; ++r) acc[r] = fmaf(qv[r][e4 * 4 + e], kv[u][e4][e], acc[r]);
+      // fixed xor tree over the 16 lanes that share row J
+#pragma unroll
+      for (int off = 1; off < 16; off <<= 1)
+#pragma unroll
+        for (int r = 0; r < QB; ++r) acc[r] = acc[r] + __shfl_xor(acc[r], off);
+      if (J < Nb && sub == 0) {
+#pragma unroll
+        for (int r = 0; r < QB; ++r)
+          if (r < nrows) p[r * Nb + J] = acc[r] * scale;
       }
-    }
-    // fixed xor tree over the 16 lanes that share row J
-#pragma unroll
-    for (int off = 1; off < 16; off <<= 1)
-#pragma unroll
-      for (int r = 0; r < QB; ++r) acc[r] = acc[r] + __shfl_xor(acc[r], off);
-    if (J < Nb && sub == 0) {
-#pragma unroll
-      for (int r = 0; r < QB; ++r)
-        if (r < nrows) p[r * Nb + J] = acc[r] * scale;
     }
   }
 }
