@@ -17,7 +17,8 @@ import torch
 __all__ = [
     "SaError", "load_library", "library_path", "Shape", "Params", "Inputs",
     "sa_abi_version", "sa_workspace_bytes", "sa_dense_workspace_bytes", "sa_pool", "sa_route",
-    "sa_forward", "sa_forward_pooled", "sa_dense_forward", "status_name",
+    "sa_forward", "sa_forward_pooled", "sa_dense_forward", "sa_qk_prologue", "status_name",
+    "Prologue", "make_params", "budget_blocks",
     "SA_F32", "SA_BF16", "SA_FP8_E4M3", "BLOCK", "MAX_NB", "MAX_N",
 ]
 
