@@ -393,6 +393,7 @@ def main() -> None:
         "pool": {"ms": pool_avg, "gbs": pool_bytes / (pool_avg * 1e-3) / 1e9,
                  "frac_hbm": pool_bytes / (pool_avg * 1e-3) / 1e9 / PEAK_HBM_GBS, "bytes": pool_bytes},
         "fused_kernel_ms": fused_avg,
+        "ms_per_call_median": float(np.median(np.add(pool_ms, fused_ms))),
         "ms_per_call_min": float(np.min(np.add(pool_ms, fused_ms))),
         "ms_per_call_p90": float(np.percentile(np.add(pool_ms, fused_ms), 90)),
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
