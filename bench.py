@@ -152,7 +152,7 @@ def main() -> None:
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: the path shards by (batch, head) with no exchange, "
-              "and runs with more than one GPU are not part of this build. Use --gpus 1.",
+              "and runs on more than one GPU are not supported. Use --gpus 1.",
               file=sys.stderr)
         sys.exit(2)
     if not torch.cuda.is_available():

@@ -67,7 +67,7 @@ typedef enum sa_status {
   SA_ERR_DTYPE = 4,       /* unsupported (qk_dtype, v_dtype) pair or scales given/missing */
   SA_ERR_ALIGN = 5,       /* pointer misaligned */
   SA_ERR_WORKSPACE = 6,   /* workspace smaller than sa_workspace_bytes() */
-  SA_ERR_UNSUPPORTED = 7, /* valid request this build does not implement */
+  SA_ERR_UNSUPPORTED = 7, /* valid request the library does not implement */
   SA_ERR_HIP = 8          /* a HIP runtime call or kernel launch failed */
 } sa_status;
 
