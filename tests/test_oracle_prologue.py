@@ -110,3 +110,9 @@ def test_prologue_means_are_block_means_of_rounded_output():
     # and y is the rounded norm + rotation
     ref = pro.apply_rope(pro.rms_norm(x, g, 1e-6), pro.rope_angles(T, Hg, Wg, D, 10000.0))
     assert np.abs(y - ref).max() <= 2.0 ** -8 * np.abs(ref).max()
+
+
+def test_rms_norm_eps_closed_form():
+    # mean square 1 and eps 3: each entry divided by sqrt(1 + 3) = 2
+    x = np.array([[1.0, -1.0, 1.0, -1.0, 1.0, -1.0]])
+    np.testing.assert_allclose(pro.rms_norm(x, np.full(6, 4.0), 3.0), 2.0 * x, rtol=1e-15)
