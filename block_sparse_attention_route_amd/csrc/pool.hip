@@ -207,8 +207,7 @@ __device__ __forceinline__ void norm_rope(u32x4 (&raw)[NP], int nrows, const flo
     float ss = 0.f;
 #pragma unroll
     for (int e = 0; e < 8; ++e) ss = fmaf(x[e], x[e], ss);
-#pragma unroll
-    for (int off = 1; off < T::CPR; off <<= 1) ss += __shfl_xor(ss, off);
+    ss = group_sum<T::CPR>(ss);
     if (r >= nrows) continue;
     const float inv = 1.0f / sqrtf(ss / (float)D + eps);
     u32x4 w;

@@ -2,6 +2,7 @@
 // vector types, bf16/fp8 conversions, LDS swizzles, the float32 routing
 // routine and small wave/workgroup reductions.  gfx950 (CDNA4, wave64) only.
 #pragma once
+#include <type_traits>
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -59,6 +60,25 @@ __device__ __forceinline__ int swz(int row, int chunk) {
   }
 }
 
+// Sum over aligned groups of L lanes (L = 2, 4, 8 or 16; a group lies inside
+// one 16-lane DPP row), every lane of a group receiving the same bits: pairs
+// (i, i^1), then (i, i^2) by quad permutation, then mirrored half-rows
+// (i, 7-i) and rows (i, 15-i).  Each step adds two equal-shaped partial sums
+// symmetrically, so the order is fixed and lane-independent; all on the
+// vector ALU (no LDS permute).
+template <int L>
+__device__ __forceinline__ float group_sum(float x) {
+  static_assert(L == 2 || L == 4 || L == 8 || L == 16, "group of 2..16 lanes");
+  auto dpp = [](float v, auto ctrl) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), decltype(ctrl)::value, 0xF, 0xF, false));
+  };
+  x += dpp(x, std::integral_constant<int, 0xB1>{});                       // quad_perm [1,0,3,2]
+  if constexpr (L >= 4) x += dpp(x, std::integral_constant<int, 0x4E>{});  // quad_perm [2,3,0,1]
+  if constexpr (L >= 8) x += dpp(x, std::integral_constant<int, 0x141>{}); // row_half_mirror
+  if constexpr (L >= 16) x += dpp(x, std::integral_constant<int, 0x140>{}); // row_mirror
+  return x;
+}
+
 __device__ __forceinline__ float wave_max(float x) {
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) x = fmaxf(x, __shfl_xor(x, off));
@@ -78,7 +98,7 @@ __device__ __forceinline__ int wave_sum_int(int x) {
 // proxy_rows() evaluates p_IJ = scale * (qbar_I . kbar_J) for QB query blocks
 // against every key block J in float32, in one fixed order: 16 lanes share a
 // key row, lane j of the 16 accumulates dims [j*D/16, (j+1)*D/16) with
-// sequential fmaf, then a fixed xor tree over the 16 lanes.  The value of a
+// sequential fmaf, then group_sum over the 16 lanes.  The value of a
 // pair (I, J) therefore does not depend on QB or on the number of threads, so
 // the standalone route kernel and every attention kernel, which all call this
 // routine, obtain identical bits.
@@ -124,11 +144,9 @@ __device__ __forceinline__ void proxy_rows(const float* __restrict__ qbar,
         for (int e = 0; e < 4; ++e)
 #pragma unroll
           for (int r = 0; r < QB; ++r) acc[r] = fmaf(qv[r][e4 * 4 + e], kv[u][e4][e], acc[r]);
-      // fixed xor tree over the 16 lanes that share row J
+      // fixed-order sum over the 16 lanes that share row J
 #pragma unroll
-      for (int off = 1; off < 16; off <<= 1)
-#pragma unroll
-        for (int r = 0; r < QB; ++r) acc[r] = acc[r] + __shfl_xor(acc[r], off);
+      for (int r = 0; r < QB; ++r) acc[r] = group_sum<16>(acc[r]);
       if (J < Nb && sub == 0) {
 #pragma unroll
         for (int r = 0; r < QB; ++r)
