@@ -36,8 +36,10 @@
 // PV operand needs.  K tiles are row-major and V tiles arrive pre-transposed
 // (d-major) from the pool step; both are copied straight from global memory
 // into a ring of LDS stages (LDS DMA, global_load_lds_dwordx4) issued one
-// tile ahead, with an XOR swizzle on 16-byte chunks that keeps the MFMA
-// operand reads free of bank conflicts.  Workgroup ids are remapped so that
+// tile ahead, from a wave-uniform base address plus per-lane offsets computed
+// once, with an XOR swizzle on 16-byte chunks that keeps the MFMA operand
+// reads free of bank conflicts; the tile loop is unrolled by ring stage so
+// that the LDS operand addresses are immediates.  Workgroup ids are remapped so that
 // each XCD works on a chunk of adjacent query blocks while all XCDs stay on
 // the same head (shared key blocks hit in that XCD's L2, the head's K/V stays
 // in the last-level cache).

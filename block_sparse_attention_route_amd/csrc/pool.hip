@@ -8,8 +8,9 @@
 // tile order of the token grid (sa_layout.h, token_of), in which case K is
 // also written out in position order.  The kernel is HBM-bound: it reads Q, K
 // and V once (each workgroup one 64-token block of one head, all three
-// tensors in flight together) and writes 1/16 as many bytes of means plus
-// the regrouped V.
+// tensors in flight together; with the producer step one block position of
+// up to eight heads, which share its rotation angles) and writes 1/16 as many
+// bytes of means plus the regrouped V.
 //
 // With the producer step fused in front (ProArgs), the rows read are the raw
 // Q/K projections: each is RMS-normalised over its D features, scaled by the
