@@ -361,12 +361,22 @@ def main() -> None:
         log(f"tile {spec}: density {tmask_np.mean():.3f}, {tms:.2f} ms")
         del wst
 
-    if args.calibrate_copy:
-        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
-        dst = torch.empty_like(src)
-        dst.copy_(src)
+    # a 1 GiB device-to-device copy: the streaming rate the HBM-bound pool is
+    # measured against (and, with --calibrate-copy, the PMC byte reference)
+    src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    copy_ms = None
+    if not args.calibrate_copy:
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(5):
+            dst.copy_(src)
+        e1.record()
         torch.cuda.synchronize()
-        del src, dst
+        copy_ms = e0.elapsed_time(e1) / 5
+    del src, dst
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -400,7 +410,8 @@ def main() -> None:
         "correction_tflop": f_corr / 1e12,
         "dense_equivalent_tflops": f_dense / (ms_step * 1e-3) / 1e12,
         "pool": {"ms": pool_avg, "gbs": pool_bytes / (pool_avg * 1e-3) / 1e9,
-                 "frac_hbm": pool_bytes / (pool_avg * 1e-3) / 1e9 / PEAK_HBM_GBS, "bytes": pool_bytes},
+                 "frac_hbm": pool_bytes / (pool_avg * 1e-3) / 1e9 / PEAK_HBM_GBS, "bytes": pool_bytes,
+                 "copy_1gib_gbs": (2 * (1 << 30) / (copy_ms * 1e-3) / 1e9) if copy_ms else None},
         "fused_kernel_ms": fused_avg,
         "ms_per_call_median": float(np.median(np.add(pool_ms, fused_ms))),
         "ms_per_call_min": float(np.min(np.add(pool_ms, fused_ms))),
