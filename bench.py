@@ -142,7 +142,7 @@ def cpu_baseline(inp, wl, tau, o_gpu, budget_s: float):
 def main() -> None:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="720p", choices=sorted(synth.WORKLOADS))
     ap.add_argument("--tau", type=float, default=None)
