@@ -263,7 +263,20 @@ def main() -> None:
         dms = e0.elapsed_time(e1) / args.dense_steps
         dense = {"ms": dms, "tflops": f_dense / (dms * 1e-3) / 1e12,
                  "frac_peak": f_dense / (dms * 1e-3) / 1e12 / peak, "sparse_speedup": dms / ms_step}
-        del wsd, od, lsed
+
+        # what the method approximates: the sparse output against dense
+        # attention on the same inputs, with the correction as configured and
+        # toggled (the error the correction of the skipped blocks removes)
+        def approx(o_s, l_s):
+            d = o_s.float() - od.float()
+            return {"o_rel_l2": float(d.norm() / od.float().norm()), "o_max_abs": float(d.abs().max()),
+                    "lse_mean_abs": float((l_s - lsed).abs().mean())}
+        o_t, l_t = api.sa_forward(q, k, v, grid, tau=tau, correction=not correction, workspace=ws,
+                                  q_scale=qs, k_scale=ks)[:2]
+        torch.cuda.synchronize()
+        dense["approx_vs_dense"] = {"tau": tau, ("correction_on" if correction else "correction_off"): approx(o, lse),
+                                    ("correction_off" if correction else "correction_on"): approx(o_t, l_t)}
+        del wsd, od, lsed, o_t, l_t
 
     # fixed-budget routing (topk blocks per query block) at the same shape
     budgets = []
