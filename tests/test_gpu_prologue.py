@@ -89,3 +89,31 @@ def test_rejects_non_bf16():
     with pytest.raises(api.SaError) as e:
         api.sa_qk_prologue(inp.q.to(dev), inp.k.to(dev), inp.v.to(dev), (1, 8, 8), g, g)
     assert e.value.status == 7
+
+
+def test_batch_and_heads_past_one_workgroup():
+    # B = 2, H = 5: ten (b, h) heads, more than the eight that one producer
+    # workgroup takes, so the second workgroup row holds only two
+    B, H, T, Hg, Wg, D = 2, 5, 2, 8, 9, 128
+    wl = synth.Workload(f"pb{B}h{H}", B, H, T, Hg, Wg, D, "bf16", (1.0,), True, seed=5)
+    say(f"case {wl.name}")
+    inp = synth.generate(wl)
+    rng = np.random.default_rng(5)
+    gq = torch.from_numpy(rng.uniform(0.5, 1.5, size=D).astype(np.float32))
+    gk = torch.from_numpy(rng.uniform(0.5, 1.5, size=D).astype(np.float32))
+    dev = torch.device("cuda:0")
+    xq, xk, v = inp.q.to(dev), inp.k.to(dev), inp.v.to(dev)
+    grid = (T, Hg, Wg)
+    q, k, ws = api.sa_qk_prologue(xq, xk, v, grid, gq.to(dev), gk.to(dev), tau=1.0)
+    torch.cuda.synchronize()
+    ang = pro.rope_angles(T, Hg, Wg, D, 10000.0)
+    for b in range(B):
+        for h in range(H):
+            for x_raw, g, y_gpu in ((inp.q, gq, q), (inp.k, gk, k)):
+                x = x_raw[b, h].to(torch.float64).numpy()
+                y_ref = pro.apply_rope(pro.rms_norm(x, g.numpy().astype(np.float64), 1e-6), ang)
+                yg = y_gpu[b, h].float().cpu().numpy().astype(np.float64)
+                assert (np.abs(yg - y_ref) <= 2.0 ** -8 * np.abs(y_ref) + 1e-5).all(), (b, h)
+    ws_pool = api.sa_pool(q, k, v, grid, tau=1.0)
+    torch.cuda.synchronize()
+    assert torch.equal(ws, ws_pool)

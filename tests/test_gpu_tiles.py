@@ -93,3 +93,8 @@ def test_fp8_with_tiles_is_rejected():
     with pytest.raises(api.SaError) as e:
         api.sa_forward(q, k, v, (wl.T, wl.Hg, wl.Wg), tau=1.0, tile=(4, 4, 4), q_scale=qs, k_scale=ks)
     assert e.value.status == 7        # SA_ERR_UNSUPPORTED
+
+
+def test_batch_of_two():
+    # CFG-like batch: heads (b, h) indexed b * H + h in every tiled buffer
+    _run(_wl(B=2, H=2, T=3, Hg=10, Wg=13), (1, 8, 8), tau=1.0)
