@@ -135,6 +135,9 @@ def cpu_baseline(inp, wl, tau, o_gpu, budget_s: float):
                    f"({t_route:.2f} s) + attention of {len(done)} query blocks incl. the ragged last one "
                    f"({t_attend:.2f} s); computed-block FLOP of the sample / time"),
         "sample_max_abs_err_vs_gpu": maxerr,
+        # the whole call at the sample's rate per query block (routing per head
+        # scaled by the heads): an extrapolation, not a measurement
+        "extrapolated_call_s": (t_route + t_attend / len(done) * len(ranges)) * wl.B * wl.H,
         "near_threshold_blocks_head0": nband,
     }
 
