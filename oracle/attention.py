@@ -34,6 +34,19 @@ The pages give no formula, so this module fixes the plainest concrete reading
 * the output is the softmax over the union of exact logits (kept blocks) and
   correction logits (skipped blocks, if correction is on), with natural-log
   LSE lse_i = M_i + ln Z_i;
+* optionally (correction = 2) the skipped blocks are modelled to first order
+  instead: PISA, as the paper review of the Sol Video Inference Engine
+  (xllm-io blog, five acceleration techniques, item "Sparse Attention")
+  describes it, computes critical blocks exactly and compensates the others
+  with a first-order Taylor approximation.  With k_j = kbar_J + d_j and q_i = qbar_I + e_i, the exact
+  weight exp(s q_i . k_j) is taken as exp(c_iJ) * (1 + s qbar_I . d_j): the
+  factor exp(c_iJ) keeps the per-row score column exactly, the bracket is the
+  first-order term in the key deviation, and the product term s e_i . d_j,
+  second order in the deviations from the block means, is dropped (with q_i in
+  place of qbar_I the first-order term would cost as much as the exact
+  block).  Because the d_j of a block sum to zero, the block's weight is still
+  n_J exp(c_iJ) and only its value changes, to
+  vbar_J + (s / n_J) sum_j (qbar_I . d_j) v_j, one vector per (I, J);
 * alternatively (route_topk) a fixed budget: each query block keeps the topk
   key blocks of largest proxy, equal proxies in increasing block order --
   the paper review of the Sol Video Inference Engine (xllm-io blog) runs
@@ -198,10 +211,12 @@ def route_topk(q: np.ndarray, k: np.ndarray, block: int, topk: int, scale: float
 
 
 def attend_rows(q_rows: np.ndarray, k: np.ndarray, v: np.ndarray, keep_row: np.ndarray,
-                block: int, correction: bool, scale: float | None = None):
+                block: int, correction, scale: float | None = None):
     """Output and LSE of the rows of one query block, given its keep row.
 
-    q_rows: [n_I, D]; k: [N, D]; v: [N, Dv]; keep_row: bool [Nb].
+    q_rows: [n_I, D], all rows of the query block; k: [N, D]; v: [N, Dv];
+    keep_row: bool [Nb].  correction: 0 / False none, 1 / True the mean
+    copies, 2 the first-order model (module docstring).
     Two passes over all logits of each row (exact logits of kept blocks, then
     the correction logits of skipped blocks with multiplicity n_J), max, sums.
     """
@@ -224,6 +239,12 @@ def attend_rows(q_rows: np.ndarray, k: np.ndarray, v: np.ndarray, keep_row: np.n
         kbar = np.stack([k[slice(*ranges[J])].mean(axis=0) for J in skipped])
         vbar = np.stack([v[slice(*ranges[J])].mean(axis=0) for J in skipped])
         nJ = np.array([ranges[J][1] - ranges[J][0] for J in skipped], dtype=np.float64)
+        if correction == 2:
+            # first order in the key deviations d_j = k_j - kbar_J, taken at qbar_I
+            qbar = q_rows.mean(axis=0)
+            for t, J in enumerate(skipped):
+                d = k[slice(*ranges[J])] - kbar[t]
+                vbar[t] = vbar[t] + (s * (d @ qbar)) @ v[slice(*ranges[J])] / nJ[t]
         c = s * (q_rows @ kbar.T)                          # score columns of skipped blocks
         logits = np.concatenate([logits, c], axis=1)
         weights_mult = np.concatenate([weights_mult, nJ])
@@ -237,7 +258,7 @@ def attend_rows(q_rows: np.ndarray, k: np.ndarray, v: np.ndarray, keep_row: np.n
     return o, lse
 
 
-def forward_head(q, k, v, block: int = 64, tau: float = math.inf, correction: bool = True,
+def forward_head(q, k, v, block: int = 64, tau: float = math.inf, correction=True,
                  scale: float | None = None, keep: np.ndarray | None = None,
                  qblocks=None, topk: int | None = None, order=None):
     """Sparse attention of one (batch, head): returns (o [N, Dv], lse [N], keep).
@@ -276,7 +297,7 @@ def forward_head(q, k, v, block: int = 64, tau: float = math.inf, correction: bo
     return o, lse, keep
 
 
-def forward(q, k, v, block: int = 64, tau: float = math.inf, correction: bool = True,
+def forward(q, k, v, block: int = 64, tau: float = math.inf, correction=True,
             scale: float | None = None, topk: int | None = None, order=None):
     """[B, H, N, D] batched form of forward_head; every (b, h) routes independently."""
     q = np.asarray(q, dtype=np.float64)
