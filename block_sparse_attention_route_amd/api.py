@@ -140,10 +140,12 @@ def make_shape(q: torch.Tensor, grid) -> Shape:
     return Shape(B, H, N, D, T, Hg, Wg)
 
 
-def make_params(tau: float, correction: bool = True, scale: float = 0.0, topk: int = 0,
+def make_params(tau: float, correction=True, scale: float = 0.0, topk: int = 0,
                 tile=None) -> Params:
+    """correction: False / 0 none, True / 1 the mean copies, 2 the first-order
+    correction (bf16 inputs)."""
     tt, th, tw = (0, 0, 0) if tile is None else (int(x) for x in tile)
-    return Params(BLOCK, float(tau), int(bool(correction)), float(scale), int(topk), tt, th, tw)
+    return Params(BLOCK, float(tau), int(correction), float(scale), int(topk), tt, th, tw)
 
 
 def budget_blocks(sparsity: float, N: int) -> int:
@@ -170,11 +172,11 @@ def sa_abi_version() -> int:
     return int(load_library().sa_abi_version())
 
 
-def sa_workspace_bytes(q, k, v, grid, q_scale=None, k_scale=None, tile=None) -> int:
+def sa_workspace_bytes(q, k, v, grid, q_scale=None, k_scale=None, tile=None, correction=True) -> int:
     lib = load_library()
     sh = make_shape(q, grid)
     inp = Inputs(None, None, None, None, None, _dtype_code(q), _dtype_code(v))
-    pr = make_params(math.inf, True, 0.0, 0, tile)
+    pr = make_params(math.inf, correction, 0.0, 0, tile)
     n = lib.sa_workspace_bytes(ctypes.byref(sh), ctypes.byref(pr), ctypes.byref(inp))
     if n == 0 and sh.B * sh.H * sh.N > 0:
         raise SaError(int(lib.sa_last_status()), lib.sa_last_error().decode() or "invalid arguments")
@@ -194,12 +196,13 @@ def _workspace(nbytes: int, like: torch.Tensor, ws: torch.Tensor | None) -> torc
     return ws
 
 
-def sa_pool(q, k, v, grid, *, tau: float = math.inf, correction: bool = True, scale: float = 0.0,
+def sa_pool(q, k, v, grid, *, tau: float = math.inf, correction=True, scale: float = 0.0,
             workspace: torch.Tensor | None = None, q_scale=None, k_scale=None, topk: int = 0,
             tile=None) -> torch.Tensor:
-    """Step pool: block means (and V regrouped per 64-key block) into the workspace."""
+    """Step pool: block means (and V regrouped per 64-key block) into the
+    workspace; with correction=2 also the first-order values."""
     lib = load_library()
-    ws = _workspace(sa_workspace_bytes(q, k, v, grid, q_scale, k_scale, tile), q, workspace)
+    ws = _workspace(sa_workspace_bytes(q, k, v, grid, q_scale, k_scale, tile, correction), q, workspace)
     sh, pr, inp = make_shape(q, grid), make_params(tau, correction, scale, topk, tile), make_inputs(q, k, v, q_scale, k_scale)
     _check(lib.sa_pool(ctypes.byref(sh), ctypes.byref(pr), ctypes.byref(inp), _ptr(ws), ws.numel(), _stream(q)))
     return ws
@@ -233,12 +236,12 @@ def _outs(q, v, out, lse, want_kept, kept):
     return out, lse, kept
 
 
-def sa_forward(q, k, v, grid, *, tau: float = math.inf, correction: bool = True, scale: float = 0.0,
+def sa_forward(q, k, v, grid, *, tau: float = math.inf, correction=True, scale: float = 0.0,
                workspace=None, q_scale=None, k_scale=None, out=None, lse=None, want_kept=False,
                kept=None, topk: int = 0, tile=None):
     """Pool + fused routed sparse attention with correction: returns (o, lse, kept or None)."""
     lib = load_library()
-    ws = _workspace(sa_workspace_bytes(q, k, v, grid, q_scale, k_scale, tile), q, workspace)
+    ws = _workspace(sa_workspace_bytes(q, k, v, grid, q_scale, k_scale, tile, correction), q, workspace)
     out, lse, kept = _outs(q, v, out, lse, want_kept, kept)
     sh, pr, inp = make_shape(q, grid), make_params(tau, correction, scale, topk, tile), make_inputs(q, k, v, q_scale, k_scale)
     _check(lib.sa_forward(ctypes.byref(sh), ctypes.byref(pr), ctypes.byref(inp), _ptr(out), _ptr(lse),
@@ -246,7 +249,7 @@ def sa_forward(q, k, v, grid, *, tau: float = math.inf, correction: bool = True,
     return out, lse, kept
 
 
-def sa_forward_pooled(q, k, v, grid, *, tau: float = math.inf, correction: bool = True, scale: float = 0.0,
+def sa_forward_pooled(q, k, v, grid, *, tau: float = math.inf, correction=True, scale: float = 0.0,
                       workspace, q_scale=None, k_scale=None, out=None, lse=None, want_kept=False,
                       kept=None, topk: int = 0, tile=None):
     """The fused kernel alone; `workspace` must hold sa_pool's output for these inputs."""
@@ -259,18 +262,19 @@ def sa_forward_pooled(q, k, v, grid, *, tau: float = math.inf, correction: bool 
 
 
 def sa_qk_prologue(xq, xk, v, grid, q_gain, k_gain, *, norm_eps: float = 1e-6, rope_base: float = 10000.0,
-                   tau: float = math.inf, topk: int = 0, tile=None, workspace=None, q_out=None, k_out=None):
+                   tau: float = math.inf, topk: int = 0, tile=None, correction=True, scale: float = 0.0,
+                   workspace=None, q_out=None, k_out=None):
     """Fused producer step: RMS norm + gain + 3-D rotary embedding of the raw
     Q/K projections (bf16) into q_out / k_out, with the pool's workspace
     filled from them.  Returns (q_out, k_out, workspace); follow with
-    sa_forward_pooled(q_out, k_out, v, ...) using the same tau/topk/tile."""
+    sa_forward_pooled(q_out, k_out, v, ...) using the same tau/topk/tile/correction/scale."""
     lib = load_library()
-    ws = _workspace(sa_workspace_bytes(xq, xk, v, grid, tile=tile), xq, workspace)
+    ws = _workspace(sa_workspace_bytes(xq, xk, v, grid, tile=tile, correction=correction), xq, workspace)
     if q_out is None:
         q_out = torch.empty_like(xq)
     if k_out is None:
         k_out = torch.empty_like(xk)
-    sh, pr, inp = make_shape(xq, grid), make_params(tau, True, 0.0, topk, tile), make_inputs(xq, xk, v)
+    sh, pr, inp = make_shape(xq, grid), make_params(tau, correction, scale, topk, tile), make_inputs(xq, xk, v)
     pro = Prologue(float(norm_eps), float(rope_base))
     _check(lib.sa_qk_prologue(ctypes.byref(sh), ctypes.byref(pr), ctypes.byref(pro), ctypes.byref(inp),
                               _ptr(q_gain), _ptr(k_gain), _ptr(q_out), _ptr(k_out), _ptr(ws), ws.numel(),

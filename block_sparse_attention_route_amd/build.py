@@ -22,7 +22,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIBDIR = os.path.join(PKG, "_lib")
 LIB = os.path.join(LIBDIR, "libsa_route.so")
 
-SOURCES = ["api.cpp", "pool.hip", "route.hip", "attn_mfma.hip", "attn_f32.hip"]
+SOURCES = ["api.cpp", "pool.hip", "route.hip", "taylor.hip", "attn_mfma.hip", "attn_f32.hip"]
 # standalone measurement programs (not part of the library)
 MICROBENCH = {"mfma_ceiling": os.path.join(PKG, "microbench", "mfma_ceiling.hip")}
 

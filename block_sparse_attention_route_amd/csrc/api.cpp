@@ -104,7 +104,9 @@ sa_status check_params(const sa_params* p, Req* r) {
   if (p->topk < 0) return fail(SA_ERR_PARAM, "topk must be >= 0 (got %d)", p->topk);
   if (p->topk == 0 && (std::isnan(p->tau) || p->tau < 0.f))
     return fail(SA_ERR_PARAM, "tau must be >= 0 or +inf");
-  if (p->correction != 0 && p->correction != 1) return fail(SA_ERR_PARAM, "correction must be 0 or 1");
+  if (p->correction < 0 || p->correction > 2) return fail(SA_ERR_PARAM, "correction must be 0, 1 or 2");
+  if (p->correction == 2 && !(r->qk == SA_BF16 && r->v == SA_BF16))
+    return fail(SA_ERR_UNSUPPORTED, "the first-order correction needs bf16 Q/K/V");
   if (!std::isfinite(p->scale)) return fail(SA_ERR_PARAM, "scale must be finite");
   const int tt = p->tile_t, th = p->tile_h, tw = p->tile_w;
   if (tt != 0 || th != 0 || tw != 0) {
@@ -115,8 +117,8 @@ sa_status check_params(const sa_params* p, Req* r) {
       return fail(SA_ERR_UNSUPPORTED, "a 3-D tile order needs bf16 or fp32 Q/K (fp8 block scales "
                   "belong to raster blocks)");
     r->tm = sa::make_tile_map(r->T, r->Hg, r->Wg, tt, th, tw);
-    r->ws = sa::ws_layout(r->BH, r->N, r->D, r->v == SA_BF16, r->dense, true);
   }
+  r->ws = sa::ws_layout(r->BH, r->N, r->D, r->v == SA_BF16, r->dense, r->tm.on != 0, p->correction == 2);
   r->tau = p->tau;
   r->topk = p->topk;
   r->correction = p->correction;
@@ -199,6 +201,7 @@ sa::AttnArgs attn_args(const Req& r, const sa_inputs* in, void* o, float* lse, i
   if (sparse) {
     a.tm = r.tm;
     if (r.tm.on && r.qk == SA_BF16) a.kpos16 = at<uint16_t>(ws, r.ws.kpos16);
+    if (r.correction == 2) a.vprime = at<uint16_t>(ws, r.ws.vprime);
   }
   a.o = o;
   a.lse = lse;
@@ -221,6 +224,34 @@ sa::AttnArgs attn_args(const Req& r, const sa_inputs* in, void* o, float* lse, i
 sa_status hip_status(hipError_t e, const char* what) {
   if (e != hipSuccess) return fail(SA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
   return ok();
+}
+
+// The first-order correction's values per (query block, key block), from the
+// pooled means in the workspace and K (token order; its position-order copy
+// is used with a 3-D tile order).
+sa_status run_taylor(const Req& r, const void* k, void* ws, hipStream_t st) {
+  sa::TaylorArgs a{};
+  a.k = static_cast<const uint16_t*>(r.tm.on ? at<uint16_t>(ws, r.ws.kpos16) : k);
+  a.qbar = at<float>(ws, r.ws.qbar);
+  a.kbar = at<float>(ws, r.ws.kbar);
+  a.vbar = at<float>(ws, r.ws.vbar);
+  a.vt16 = at<uint16_t>(ws, r.ws.vt16);
+  a.vprime = at<uint16_t>(ws, r.ws.vprime);
+  a.BH = (int)r.BH;
+  a.N = (int)r.N;
+  a.Nb = (int)r.Nb;
+  a.Nbp = (int)r.Nbp;
+  a.D = r.D;
+  a.scale = r.scale;
+  return hip_status(sa::launch_taylor(a, st), "first-order values kernel launch");
+}
+
+// Pool step, followed by the first-order values when that correction is on.
+sa_status run_pool(const Req& r, const sa_inputs* in, void* ws, hipStream_t st) {
+  sa_status s;
+  if ((s = hip_status(sa::launch_pool(pool_args(r, in, ws, false), st), "pool kernel launch")) != SA_OK)
+    return s;
+  return r.correction == 2 ? run_taylor(r, in->k, ws, st) : s;
 }
 
 sa_status run_attn(const Req& r, const sa_inputs* in, void* o, float* lse, int32_t* kept, void* ws,
@@ -278,8 +309,7 @@ SA_API sa_status sa_pool(const sa_shape* shape, const sa_params* params, const s
   if ((s = check_params(params, &r)) != SA_OK) return s;
   if (r.empty) return ok();
   if ((s = check_ws(ws, ws_bytes, r)) != SA_OK) return s;
-  return hip_status(sa::launch_pool(pool_args(r, in, ws, false), (hipStream_t)stream),
-                    "pool kernel launch");
+  return run_pool(r, in, ws, (hipStream_t)stream);
 }
 
 SA_API sa_status sa_route(const sa_shape* shape, const sa_params* params, const sa_inputs* in,
@@ -333,8 +363,7 @@ SA_API sa_status sa_forward(const sa_shape* shape, const sa_params* params, cons
   if ((s = check_out(o, lse, kept)) != SA_OK) return s;
   if ((s = check_ws(ws, ws_bytes, r)) != SA_OK) return s;
   hipStream_t st = (hipStream_t)stream;
-  if ((s = hip_status(sa::launch_pool(pool_args(r, in, ws, false), st), "pool kernel launch")) != SA_OK)
-    return s;
+  if ((s = run_pool(r, in, ws, st)) != SA_OK) return s;
   return run_attn(r, in, o, lse, kept, ws, true, st);
 }
 
@@ -367,7 +396,8 @@ SA_API sa_status sa_qk_prologue(const sa_shape* shape, const sa_params* params, 
   a.pro.T = r.T;
   a.pro.Hg = r.Hg;
   a.pro.Wg = r.Wg;
-  return hip_status(sa::launch_pool(a, (hipStream_t)stream), "producer kernel launch");
+  if ((s = hip_status(sa::launch_pool(a, (hipStream_t)stream), "producer kernel launch")) != SA_OK) return s;
+  return r.correction == 2 ? run_taylor(r, k_out, ws, (hipStream_t)stream) : s;
 }
 
 SA_API sa_status sa_dense_forward(const sa_shape* shape, float scale, const sa_inputs* in, void* o,

@@ -76,12 +76,6 @@ __device__ __forceinline__ float xor32_max(float x) {
   return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
-// Key row that MFMA row m of a 32-key tile reads: swap bits 2 and 3.
-__device__ __forceinline__ int kperm(int m) { return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1); }
-
-// Key (within a 32-key tile) of accumulator element r of S^T, lane half h.
-__device__ __forceinline__ int key_of(int r, int h) { return r < 8 ? 8 * h + r : 8 + 8 * h + r; }
-
 template <int CPR>
 __device__ __forceinline__ int swz_any(int row, int chunk) {
   if constexpr (CPR == 4) {
@@ -196,7 +190,7 @@ __device__ __forceinline__ void wait_tiles_ahead(int ahead) {
   wait_vmcnt<0>();
 }
 
-template <int D, bool SPARSE, bool FP8, int QB, int ST>
+template <int D, bool SPARSE, bool FP8, int QB, int ST, bool TAY = false>
 __global__ __launch_bounds__(128 * QB, QB == 2 ? 2 : 1) void attn_kernel(AttnArgs a) {
   using C = Cfg<D>;
   constexpr int NT = 128 * QB;        // threads
@@ -209,6 +203,7 @@ __global__ __launch_bounds__(128 * QB, QB == 2 ? 2 : 1) void attn_kernel(AttnArg
   constexpr int SMEM_PROXY = SPARSE ? QB * kMaxNb * 4 : 0;
   constexpr int SMEM = SMEM_STAGE > SMEM_PROXY ? SMEM_STAGE : SMEM_PROXY;
   static_assert(KI8 >= 1 && VI >= 1, "tile copies per wave");
+  static_assert(!TAY || (SPARSE && !FP8), "first-order values: sparse bf16 only");
 
   __shared__ __attribute__((aligned(1024))) uint8_t smem[SMEM];
   __shared__ uint8_t flags[SPARSE ? kMaxNb : 1];
@@ -221,6 +216,9 @@ __global__ __launch_bounds__(128 * QB, QB == 2 ? 2 : 1) void attn_kernel(AttnArg
   __shared__ int hist[SPARSE ? QB * 256 : 1];
   __shared__ uint32_t sel[SPARSE ? 3 * QB : 1];
   __shared__ int nunion_s;
+  // correction mode 2: the first-order value tile of each query block, 64 key
+  // rows of D bf16, unswizzled (operands are gathered from it per element)
+  __shared__ __attribute__((aligned(16))) uint8_t vps[TAY ? QB * C::KTILE : 1];
 
   const int N = a.N, Nb = a.Nb;
   const int ngroups = (Nb + QB - 1) / QB;
@@ -381,6 +379,21 @@ __global__ __launch_bounds__(128 * QB, QB == 2 ? 2 : 1) void attn_kernel(AttnArg
     }
   };
 
+  // First-order values of correction tile `it` for this wave's query block:
+  // rows [64 it, 64 it + 64) of V'[I] (16 KiB contiguous at D = 128), half a
+  // tile per wave, issued before the next ring tile so that waiting for them
+  // leaves that tile in flight.
+  const uint32_t vps_base = (uint32_t)(uintptr_t)vps;
+  auto issue_vprime = [&](int it) {
+    constexpr int VPW = C::KTILE / 1024 / 2;
+    const uint8_t* tile = reinterpret_cast<const uint8_t*>(a.vprime + (((size_t)bh * Nb + I) * a.Nbp + 64 * it) * D) +
+                          qhalf * (C::KTILE / 2);
+    const uint32_t off = 16 * lane;
+#pragma unroll
+    for (int i = 0; i < VPW; ++i)
+      dma16s(off, uniform_addr(tile + 1024 * i), vps_base + qsel * C::KTILE + qhalf * (C::KTILE / 2) + 1024 * i);
+  };
+
   // ----------------------------------------------------- online-softmax state
   f32x16 acc[C::DT];
 #pragma unroll
@@ -407,16 +420,33 @@ __global__ __launch_bounds__(128 * QB, QB == 2 ? 2 : 1) void attn_kernel(AttnArg
     const int stg = STG >= 0 ? STG : it % ST;
     wait_tiles_ahead<LPT, ST - 2>(min(ST - 2, ntiles - 1 - it));
     __syncthreads();
-    if (it + ST - 1 < ntiles) issue_tile(it + ST - 1, STG >= 0 ? (STG + ST - 1) % ST : (it + ST - 1) % ST);
-
     constexpr bool virt = KIND == kVirt;
+    constexpr bool tv = TAY && virt;   // correction tile with first-order values
+    if constexpr (tv) {
+      if (qvalid) issue_vprime(it);
+    }
+    const bool ahead = it + ST - 1 < ntiles;
+    if (ahead) issue_tile(it + ST - 1, STG >= 0 ? (STG + ST - 1) % ST : (it + ST - 1) % ST);
+    // the value tile has landed (loads complete in order) and is visible to
+    // both waves of the query block; every wave takes part
+    auto values_ready = [&]() __attribute__((always_inline)) {
+      if (ahead)
+        wait_vmcnt<LPT>();
+      else
+        wait_vmcnt<0>();
+      __syncthreads();
+    };
+
     int J = 0;
     bool active = qvalid;
     if (!virt) {
       J = __builtin_amdgcn_readfirstlane(tile_block(it));
       if constexpr (SPARSE) active = active && ((ulist[it - nvirt] >> (12 + qsel)) & 1);
     }
-    if (!active) return;
+    if (!active) {
+      if constexpr (tv) values_ready();
+      return;
+    }
 
     // ---- S^T = K Q^T for the 64 keys of the tile (two 32-key MFMA tiles)
     const uint8_t* Kb = smem + stg * C::STAGE;
@@ -546,13 +576,30 @@ __global__ __launch_bounds__(128 * QB, QB == 2 ? 2 : 1) void attn_kernel(AttnArg
     l_run += rs;
 
     // ---- O^T += V^T P^T
+    if constexpr (tv) {
+      // first-order values: key rows in LDS, gathered 8 keys per operand
+      values_ready();
+      // lane: value column d = 32 dt + l32 of keys 16 k4 + 8 h + e
+      const __bf16* vq = reinterpret_cast<const __bf16*>(vps + qsel * C::KTILE) + 8 * h * D + l32;
 #pragma unroll
-    for (int dt = 0; dt < C::DT; ++dt) {
-      const int vrow = 32 * dt + l32;
+      for (int dt = 0; dt < C::DT; ++dt) {
 #pragma unroll
-      for (int k4 = 0; k4 < 4; ++k4) {
-        const bf16x8 va = *reinterpret_cast<const bf16x8*>(Vb + vrow * 128 + swz<8>(vrow, 2 * k4 + h) * 16);
-        acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[k4], acc[dt], 0, 0, 0);
+        for (int k4 = 0; k4 < 4; ++k4) {
+          bf16x8 va;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) va[e] = vq[(16 * k4 + e) * D + 32 * dt];
+          acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[k4], acc[dt], 0, 0, 0);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int dt = 0; dt < C::DT; ++dt) {
+        const int vrow = 32 * dt + l32;
+#pragma unroll
+        for (int k4 = 0; k4 < 4; ++k4) {
+          const bf16x8 va = *reinterpret_cast<const bf16x8*>(Vb + vrow * 128 + swz<8>(vrow, 2 * k4 + h) * 16);
+          acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[k4], acc[dt], 0, 0, 0);
+        }
       }
     }
     };
@@ -615,6 +662,12 @@ hipError_t launch_d(const AttnArgs& a, hipStream_t st) {
   constexpr int STG = SA_STAGES;
   const int ngroups = (a.Nb + QB - 1) / QB;
   const dim3 grid((unsigned)(a.BH * ngroups));
+  if constexpr (!FP8) {
+    if (a.sparse && a.vprime) {
+      hipLaunchKernelGGL((attn_kernel<D, true, false, QB, STG, true>), grid, dim3(128 * QB), 0, st, a);
+      return hipGetLastError();
+    }
+  }
   if (a.sparse)
     hipLaunchKernelGGL((attn_kernel<D, true, FP8, QB, STG>), grid, dim3(128 * QB), 0, st, a);
   else

@@ -47,6 +47,15 @@ __device__ __forceinline__ float fp8e4m3_to_f32(uint32_t byte) {
   return __uint_as_float(__float_as_uint(mag) | s);
 }
 
+// S^T = K Q^T with v_mfma_f32_32x32x16_bf16 (one query per lane column),
+// followed by O^T = V^T P^T: if MFMA row m of a 32-key tile reads key row
+// kperm(m) (bits 2 and 3 swapped), the keys a lane holds in its S^T
+// accumulators are exactly the keys of its B operand in the PV product.
+__device__ __forceinline__ int kperm(int m) { return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1); }
+
+// Key (within a 32-key tile) of accumulator element r of S^T, lane half h.
+__device__ __forceinline__ int key_of(int r, int h) { return r < 8 ? 8 * h + r : 8 + 8 * h + r; }
+
 // Position of a 16-byte chunk in an LDS row, XOR-swizzled so that 16 lanes
 // reading the same logical chunk of 16 consecutive rows hit distinct banks.
 // chunks_per_row is 16 (256-byte rows) or 8 (128-byte rows).

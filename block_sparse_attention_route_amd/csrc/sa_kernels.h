@@ -44,6 +44,18 @@ struct PoolArgs {
   ProArgs pro;           // producer step fused in front (pro.on)
 };
 
+// First-order values of the skipped blocks (correction mode 2, bf16 only).
+struct TaylorArgs {
+  const uint16_t* k;     // [BH][N][D] bf16 K in position order (the caller's K, or kpos16)
+  const float* qbar;     // [BH][Nb][D]
+  const float* kbar;
+  const float* vbar;
+  const uint16_t* vt16;  // [BH][Nb][D][64]
+  uint16_t* vprime;      // [BH][Nb][Nbp][D]
+  int BH, N, Nb, Nbp, D;
+  float scale;           // softmax scale s
+};
+
 struct RouteArgs {
   const float* qbar;
   const float* kbar;
@@ -68,6 +80,7 @@ struct AttnArgs {
   const uint16_t* vt16;
   TileMap tm;            // position -> token order (on == 0: raster)
   const uint16_t* kpos16;  // K in position order when tm.on (bf16 K)
+  const uint16_t* vprime;  // correction mode 2: first-order values, else null
   void* o;
   float* lse;
   int32_t* kept;
@@ -82,6 +95,7 @@ struct AttnArgs {
 
 hipError_t launch_pool(const PoolArgs& a, hipStream_t st);
 hipError_t launch_route(const RouteArgs& a, hipStream_t st);
+hipError_t launch_taylor(const TaylorArgs& a, hipStream_t st);
 hipError_t launch_attn_mfma(const AttnArgs& a, hipStream_t st);
 hipError_t launch_attn_f32(const AttnArgs& a, hipStream_t st);
 

@@ -11,6 +11,9 @@
 //                                     transposed (d-major), keys >= N zero (bf16 V only)
 //   kpos16  bf16  [BH][N][D]          K in block (position) order; only with a
 //                                     3-D tile order (bf16 K only)
+//   vprime  bf16  [BH][Nb][Nbp][D]    first-order values of the skipped blocks,
+//                                     per query block I and key block J, rows
+//                                     J >= Nb zero; only with correction mode 2
 //
 // The dense path uses only vt16.  Blocks are formed over positions: position
 // i is token i in the raster order, or token_of(i) in the 3-D tile order.
@@ -25,7 +28,7 @@ constexpr int kBlock = 64;
 constexpr int kMaxNb = 4096;
 
 struct WsLayout {
-  size_t qbar, kbar, vbar, kbar16, vbarT16, vt16, kpos16, total;
+  size_t qbar, kbar, vbar, kbar16, vbarT16, vt16, kpos16, vprime, total;
 };
 
 // Position -> token map of the 3-D tile order.  Full tiles of tt x th x tw =
@@ -91,7 +94,7 @@ __host__ __device__ inline int token_of(const TileMap& m, int pos) {
 __host__ __device__ inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 __host__ __device__ inline WsLayout ws_layout(int64_t BH, int64_t N, int64_t D, bool v_bf16,
-                                              bool dense_only, bool tiled = false) {
+                                              bool dense_only, bool tiled = false, bool first_order = false) {
   const int64_t Nb = (N + kBlock - 1) / kBlock;
   const int64_t Nbp = (Nb + 63) / 64 * 64;
   WsLayout L{};
@@ -112,6 +115,7 @@ __host__ __device__ inline WsLayout ws_layout(int64_t BH, int64_t N, int64_t D, 
   }
   if (v_bf16) L.vt16 = take((size_t)(BH * Nb * D * kBlock) * 2);
   if (tiled && v_bf16 && !dense_only) L.kpos16 = take((size_t)(BH * N * D) * 2);
+  if (first_order && v_bf16 && !dense_only) L.vprime = take((size_t)BH * Nb * Nbp * D * 2);
   L.total = off;
   return L;
 }

@@ -1,0 +1,246 @@
+// First-order values of the skipped blocks (correction mode 2) for gfx950.
+//
+// Paper review of the Sol Video Inference Engine (xllm-io blog, five
+// acceleration techniques, item "Sparse Attention"): PISA computes the
+// critical blocks exactly and compensates the others with a first-order
+// Taylor approximation.  Expanding the weight exp(s q_i . k_j) of a key of a
+// skipped block J to first order in the key's deviation d_j = k_j - kbar_J,
+// with the coefficient taken at the query block mean qbar_I (the product of
+// the query's and the key's deviations is second order and dropped), leaves
+// the block's weight n_J exp(s q_i . kbar_J) as it is and replaces its value
+// by
+//
+//   V'[I][J] = vbar_J + (s / n_J) * sum_{j in J} (qbar_I . d_j) v_j,
+//
+// one D-vector per (query block, key block).  This kernel writes all of them,
+// bf16, [BH][Nb][Nbp][D], rows J >= Nb zero; the fused attention kernel then
+// reads rows [I][64c, 64c + 64) as the values of correction tile c.
+//
+// Workgroup: one head, 128 query blocks (four waves of 32, one per lane
+// column) and one chunk of 64 key blocks.  For each key block J it computes,
+// like an attention tile with the block means as queries,
+//   S^T = K_J Qbar^T       v_mfma_f32_32x32x16_bf16 on bf16(qbar_I)
+//   S~  = S^T - r_IJ       r_IJ = bf16(qbar_I) . kbar_J in fp32: centred
+//                          scores, whose sum over the block vanishes; keys
+//                          past the end of the sequence give 0
+//   U^T = V_J^T bf16(S~)   the same MFMA, V_J^T from the regrouped V
+// and writes vbar_J + (s / n_J) U.  The K and V^T tiles of the next key block
+// are fetched into registers while the current one is used and handed over
+// through a second LDS buffer, so one barrier per key block suffices.
+#include "sa_device.h"
+#include "sa_kernels.h"
+
+namespace sa {
+namespace {
+
+constexpr int kTyWaves = 4;             // waves per workgroup
+constexpr int kTyRows = 32 * kTyWaves;  // query blocks per workgroup
+constexpr int kTyThreads = 64 * kTyWaves;
+
+template <int D>
+struct TyCfg {
+  static constexpr int KS = D / 16;           // k-steps of S^T
+  static constexpr int DT = D / 32;           // 32-row d tiles of U^T
+  static constexpr int KROW = 2 * D;          // bytes of a bf16 K row
+  static constexpr int CPR = KROW / 16;       // 16-byte chunks per K row
+  static constexpr int KTILE = 64 * KROW;     // K tile: 64 keys
+  static constexpr int VTILE = D * 128;       // V^T tile: D rows of 64 bf16 keys
+  static constexpr int KLD = KTILE / 16 / kTyThreads;  // 16-byte copies per thread
+  static constexpr int VLD = VTILE / 16 / kTyThreads;
+};
+
+template <int D>
+__global__ __launch_bounds__(kTyThreads, 2) void taylor_kernel(TaylorArgs a) {
+  using C = TyCfg<D>;
+  static_assert(C::KLD >= 1 && C::VLD >= 1, "tile copies per thread");
+  __shared__ __attribute__((aligned(16))) uint8_t kt[2][C::KTILE];
+  __shared__ __attribute__((aligned(16))) uint8_t vt[2][C::VTILE];
+  __shared__ __attribute__((aligned(16))) float kb[2][D];
+  __shared__ __attribute__((aligned(16))) float vb[2][D];
+
+  const int N = a.N, Nb = a.Nb, Nbp = a.Nbp;
+  const int nit = (Nb + kTyRows - 1) / kTyRows;
+  const int nch = Nbp / 64;
+  const int G = a.BH * nch * nit;
+  const int t = xcd_remap<16>((int)blockIdx.x, G);
+  const int bh = t / (nch * nit);
+  const int rem = t - bh * (nch * nit);
+  const int ch = rem / nit, itile = rem - ch * nit;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int h = lane >> 5, l32 = lane & 31;
+  const int I = kTyRows * itile + 32 * wave + l32;   // this lane's query block
+  const bool ivalid = I < Nb;
+  const int J0 = 64 * ch;
+  const int Jend = min(J0 + 64, Nb);                  // key blocks with data
+  const int ntail = N - (Nb - 1) * kBlock;
+
+  // bf16(qbar_I): the B operand of S^T
+  bf16x8 qr[C::KS];
+#pragma unroll
+  for (int ks = 0; ks < C::KS; ++ks) {
+    bf16x8 x = {};
+    if (ivalid) {
+      const float* src = a.qbar + ((size_t)bh * Nb + I) * D + 16 * ks + 8 * h;
+      const f32x4 lo = *reinterpret_cast<const f32x4*>(src);
+      const f32x4 hi = *reinterpret_cast<const f32x4*>(src + 4);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        x[e] = static_cast<__bf16>(lo[e]);
+        x[e + 4] = static_cast<__bf16>(hi[e]);
+      }
+    }
+    qr[ks] = x;
+  }
+
+  // Copies of key block J: per thread KLD + VLD 16-byte chunks of the K and
+  // V^T tiles, and one of the kbar / vbar rows for the first D/2 threads.
+  u32x4 kr[C::KLD], vr[C::VLD], mr;
+  auto fetch = [&](int J) {
+    const int nJ = (J == Nb - 1) ? ntail : kBlock;
+    const uint16_t* kbase = a.k + ((size_t)bh * N + (size_t)J * kBlock) * D;
+#pragma unroll
+    for (int i = 0; i < C::KLD; ++i) {
+      const int P = tid + kTyThreads * i, row = P / C::CPR, pc = P % C::CPR;
+      const int src_row = min(row, nJ - 1);   // rows past the sequence end: finite data, zeroed later
+      kr[i] = *reinterpret_cast<const u32x4*>(kbase + (size_t)src_row * D + swz<C::CPR>(row, pc) * 8);
+    }
+    const uint16_t* vbase = a.vt16 + ((size_t)bh * Nb + J) * D * kBlock;
+#pragma unroll
+    for (int i = 0; i < C::VLD; ++i) {
+      const int P = tid + kTyThreads * i, row = P / 8, pc = P % 8;
+      vr[i] = *reinterpret_cast<const u32x4*>(vbase + row * 64 + swz<8>(row, pc) * 8);
+    }
+    if (tid < D / 2) {
+      const float* m = (tid < D / 4 ? a.kbar : a.vbar) + ((size_t)bh * Nb + J) * D + 4 * (tid % (D / 4));
+      mr = *reinterpret_cast<const u32x4*>(m);
+    }
+  };
+  auto stash = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < C::KLD; ++i) {
+      const int P = tid + kTyThreads * i;
+      *reinterpret_cast<u32x4*>(&kt[buf][16 * P]) = kr[i];
+    }
+#pragma unroll
+    for (int i = 0; i < C::VLD; ++i) {
+      const int P = tid + kTyThreads * i;
+      *reinterpret_cast<u32x4*>(&vt[buf][16 * P]) = vr[i];
+    }
+    if (tid < D / 2) {
+      float* m = (tid < D / 4 ? kb[buf] : vb[buf]) + 4 * (tid % (D / 4));
+      *reinterpret_cast<u32x4*>(m) = mr;
+    }
+  };
+
+  if (J0 < Jend) {
+    fetch(J0);
+    stash(0);
+  }
+  __syncthreads();
+
+  const float s = a.scale;
+  for (int j = 0; j < 64; ++j) {
+    const int J = J0 + j, buf = j & 1;
+    const bool more = J + 1 < Jend;
+    if (more) fetch(J + 1);
+    uint16_t* orow = a.vprime + (((size_t)bh * Nb + (ivalid ? I : 0)) * Nbp + J) * D;
+    if (J < Jend) {
+      const uint8_t* Kb = kt[buf];
+      const uint8_t* Vb = vt[buf];
+      // r_IJ = bf16(qbar_I) . kbar_J: this lane's half of d, plus lane^32's
+      float rp = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < C::KS; ++ks) {
+        const f32x4 lo = *reinterpret_cast<const f32x4*>(&kb[buf][16 * ks + 8 * h]);
+        const f32x4 hi = *reinterpret_cast<const f32x4*>(&kb[buf][16 * ks + 8 * h + 4]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          rp = fmaf(static_cast<float>(qr[ks][e]), lo[e], rp);
+          rp = fmaf(static_cast<float>(qr[ks][e + 4]), hi[e], rp);
+        }
+      }
+      const float r = rp + __shfl_xor(rp, 32);
+
+      // S^T = K_J Qbar^T
+      f32x16 sc[2];
+#pragma unroll
+      for (int k2 = 0; k2 < 2; ++k2)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) sc[k2][e] = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < C::KS; ++ks) {
+#pragma unroll
+        for (int k2 = 0; k2 < 2; ++k2) {
+          const int krow = 32 * k2 + kperm(l32);
+          const bf16x8 ka = *reinterpret_cast<const bf16x8*>(Kb + krow * C::KROW + swz<C::CPR>(krow, 2 * ks + h) * 16);
+          sc[k2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qr[ks], sc[k2], 0, 0, 0);
+        }
+      }
+      // centred scores in bf16, the B operand of U^T; keys past the sequence end give 0
+      const int nJ = (J == Nb - 1) ? ntail : kBlock;
+      bf16x8 pb[4];
+#pragma unroll
+      for (int k2 = 0; k2 < 2; ++k2)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const bool live = 32 * k2 + key_of(e, h) < nJ;
+          pb[2 * k2 + (e >> 3)][e & 7] = static_cast<__bf16>(live ? sc[k2][e] - r : 0.f);
+        }
+
+      // U^T = V_J^T S~^T, then vbar_J + (s / n_J) U
+      const float coef = s / (float)nJ;
+#pragma unroll
+      for (int dt = 0; dt < C::DT; ++dt) {
+        const int vrow = 32 * dt + l32;
+        f32x16 acc;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc[e] = 0.f;
+#pragma unroll
+        for (int k4 = 0; k4 < 4; ++k4) {
+          const bf16x8 va = *reinterpret_cast<const bf16x8*>(Vb + vrow * 128 + swz<8>(vrow, 2 * k4 + h) * 16);
+          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[k4], acc, 0, 0, 0);
+        }
+        if (ivalid) {
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const int d = 32 * dt + 8 * g + 4 * h;
+            const f32x4 vm = *reinterpret_cast<const f32x4*>(&vb[buf][d]);
+            u32x2 w;
+            w[0] = (uint32_t)f32_to_bf16_bits(fmaf(coef, acc[4 * g + 0], vm[0])) |
+                   ((uint32_t)f32_to_bf16_bits(fmaf(coef, acc[4 * g + 1], vm[1])) << 16);
+            w[1] = (uint32_t)f32_to_bf16_bits(fmaf(coef, acc[4 * g + 2], vm[2])) |
+                   ((uint32_t)f32_to_bf16_bits(fmaf(coef, acc[4 * g + 3], vm[3])) << 16);
+            *reinterpret_cast<u32x2*>(orow + d) = w;
+          }
+        }
+      }
+    } else if (ivalid) {
+      // key blocks J >= Nb: zero rows (the attention kernel masks them, but
+      // reads them as MFMA operands)
+      const u32x2 z = {0u, 0u};
+#pragma unroll
+      for (int dt = 0; dt < C::DT; ++dt)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) *reinterpret_cast<u32x2*>(orow + 32 * dt + 8 * g + 4 * h) = z;
+    }
+    if (more) stash(buf ^ 1);
+    __syncthreads();
+  }
+}
+
+template <int D>
+hipError_t launch_d(const TaylorArgs& a, hipStream_t st) {
+  const int nit = (a.Nb + kTyRows - 1) / kTyRows;
+  const dim3 grid((unsigned)(a.BH * (a.Nbp / 64) * nit));
+  hipLaunchKernelGGL(taylor_kernel<D>, grid, dim3(kTyThreads), 0, st, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_taylor(const TaylorArgs& a, hipStream_t st) {
+  if (a.BH == 0 || a.Nb == 0) return hipSuccess;
+  return a.D == 64 ? launch_d<64>(a, st) : launch_d<128>(a, st);
+}
+
+}  // namespace sa

@@ -89,7 +89,18 @@ typedef struct sa_shape {
 /* Routing parameters (Sol-Attn page, "Abstract": query-dependent threshold).
  * block: must be 64.  tau: threshold below the row maximum of the proxy, in
  * scaled-logit (natural log) units; tau >= 0, +INFINITY keeps every block.
- * correction: 1 = add the skipped-block correction, 0 = drop skipped blocks.
+ * correction: 1 = add the skipped-block correction (each skipped block as n_J
+ * copies of its mean key and mean value), 0 = drop skipped blocks, 2 = the
+ * first-order correction: PISA compensates non-critical blocks with a
+ * first-order Taylor approximation (paper review of the Sol Video Inference
+ * Engine, xllm-io blog, five acceleration techniques, item "Sparse
+ * Attention").  Read here as the expansion of exp(s q_i . k_j) to first order
+ * in the key's deviation d_j = k_j - kbar_J, coefficient taken at the query
+ * block mean: a skipped block keeps the weight n_J exp(s q_i . kbar_J) and
+ * takes the value vbar_J + (s / n_J) sum_j (qbar_I . d_j) v_j.  Needs bf16
+ * Q/K/V (otherwise SA_ERR_UNSUPPORTED); the pool step then also writes these
+ * values, one D-vector per (query block, key block), and the workspace grows
+ * by B*H*Nb*Nbp*D bf16 (Nbp = Nb rounded up to 64).
  * scale: softmax scale s; <= 0 selects 1/sqrt(D); must be finite.
  * topk: 0 = threshold routing with tau; > 0 = fixed budget instead: every
  * query block keeps the min(topk, Nb) key blocks of largest proxy, equal
@@ -159,7 +170,8 @@ size_t sa_workspace_bytes(const sa_shape* shape, const sa_params* params, const 
 /* Step "pool" (the pooled score's operands): writes qbar, kbar, vbar (fp32
  * means over each block's actual n_J tokens; fp8 inputs are dequantised with
  * their block scale) and the regrouped V used by the attention kernels into
- * the workspace. */
+ * the workspace; with params->correction == 2 also the first-order values of
+ * every (query block, key block) pair. */
 sa_status sa_pool(const sa_shape* shape, const sa_params* params, const sa_inputs* in,
                   void* ws, size_t ws_bytes, void* stream);
 

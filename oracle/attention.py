@@ -77,6 +77,7 @@ __all__ = [
     "route",
     "route_topk",
     "tile_order",
+    "first_order_value",
     "attend_rows",
     "forward_head",
     "forward",
@@ -210,6 +211,19 @@ def route_topk(q: np.ndarray, k: np.ndarray, block: int, topk: int, scale: float
     return keep, p, pk
 
 
+def first_order_value(qbar: np.ndarray, kJ: np.ndarray, vJ: np.ndarray, s: float) -> np.ndarray:
+    """Value of a skipped key block under the first-order model (module
+    docstring): vbar_J + (s / n_J) sum_j (qbar_I . (k_j - kbar_J)) v_j.
+
+    qbar: [D] mean of the query block; kJ: [n_J, D], vJ: [n_J, Dv] the block's
+    keys and values; s: the softmax scale.
+    """
+    kJ = np.asarray(kJ, dtype=np.float64)
+    vJ = np.asarray(vJ, dtype=np.float64)
+    d = kJ - kJ.mean(axis=0)                  # key deviations from the block mean
+    return vJ.mean(axis=0) + (s * (d @ np.asarray(qbar, dtype=np.float64))) @ vJ / kJ.shape[0]
+
+
 def attend_rows(q_rows: np.ndarray, k: np.ndarray, v: np.ndarray, keep_row: np.ndarray,
                 block: int, correction, scale: float | None = None):
     """Output and LSE of the rows of one query block, given its keep row.
@@ -240,11 +254,9 @@ def attend_rows(q_rows: np.ndarray, k: np.ndarray, v: np.ndarray, keep_row: np.n
         vbar = np.stack([v[slice(*ranges[J])].mean(axis=0) for J in skipped])
         nJ = np.array([ranges[J][1] - ranges[J][0] for J in skipped], dtype=np.float64)
         if correction == 2:
-            # first order in the key deviations d_j = k_j - kbar_J, taken at qbar_I
             qbar = q_rows.mean(axis=0)
             for t, J in enumerate(skipped):
-                d = k[slice(*ranges[J])] - kbar[t]
-                vbar[t] = vbar[t] + (s * (d @ qbar)) @ v[slice(*ranges[J])] / nJ[t]
+                vbar[t] = first_order_value(qbar, k[slice(*ranges[J])], v[slice(*ranges[J])], s)
         c = s * (q_rows @ kbar.T)                          # score columns of skipped blocks
         logits = np.concatenate([logits, c], axis=1)
         weights_mult = np.concatenate([weights_mult, nJ])

@@ -94,7 +94,8 @@ def test_bad_shapes(lib, kw, code):
     (dict(block=32), "SA_ERR_PARAM"),
     (dict(tau=-1.0), "SA_ERR_PARAM"),
     (dict(tau=math.nan), "SA_ERR_PARAM"),
-    (dict(corr=2), "SA_ERR_PARAM"),
+    (dict(corr=3), "SA_ERR_PARAM"),
+    (dict(corr=-1), "SA_ERR_PARAM"),
     (dict(scale=math.inf), "SA_ERR_PARAM"),
     (dict(topk=-1), "SA_ERR_PARAM"),
     (dict(topk=-5, tau=math.nan), "SA_ERR_PARAM"),
@@ -170,6 +171,26 @@ def test_tile_order_with_fp8_is_unsupported(lib):
     inp = _inputs(qk=api.SA_FP8_E4M3, v=api.SA_BF16, qs=FAKE, ks=FAKE)
     st = _fwd(lib, _shape(), _params(tile=(4, 4, 4)), inp)
     assert api.status_name(st) == "SA_ERR_UNSUPPORTED"
+
+
+@pytest.mark.parametrize("qk,v,scales", [
+    (api.SA_FP8_E4M3, api.SA_BF16, True),
+    (api.SA_F32, api.SA_F32, False),
+])
+def test_first_order_correction_needs_bf16(lib, qk, v, scales):
+    inp = _inputs(qk=qk, v=v, qs=FAKE if scales else None, ks=FAKE if scales else None)
+    assert api.status_name(_fwd(lib, _shape(), _params(corr=2), inp)) == "SA_ERR_UNSUPPORTED"
+
+
+def test_first_order_workspace_holds_values_per_block_pair(lib):
+    sh = _shape(B=2, H=3, T=1, Hg=10, Wg=13, D=128)     # N = 130: Nb = 3, Nbp = 64
+    n1 = lib.sa_workspace_bytes(ctypes.byref(sh), ctypes.byref(_params()), ctypes.byref(_inputs()))
+    n2 = lib.sa_workspace_bytes(ctypes.byref(sh), ctypes.byref(_params(corr=2)), ctypes.byref(_inputs()))
+    assert n2 - n1 == (6 * 3 * 64 * 128 * 2 + 255) // 256 * 256
+    # with the 3-D tile order both copies are there
+    n3 = lib.sa_workspace_bytes(ctypes.byref(sh), ctypes.byref(_params(corr=2, tile=(1, 8, 8))),
+                                ctypes.byref(_inputs()))
+    assert n3 - n2 == (6 * 130 * 128 * 2 + 255) // 256 * 256
 
 
 def test_tiled_workspace_holds_k_in_tile_order(lib):

@@ -1,0 +1,186 @@
+"""GPU parity of the first-order correction (correction = 2) against the CPU
+oracle.
+
+* seeded cases spanning several tiles and a ragged tail: D = 128 and 64,
+  threshold and fixed budget, raster and 3-D tile order, batch and heads
+  above one, explicit scale: masks and every row's O and LSE against the
+  oracle's first-order model;
+* the first-order values themselves (the section sa_pool appends to the
+  workspace) against oracle.first_order_value for every (query block, key
+  block) pair of a case, padding rows zero;
+* LSE against the mean copies' run on the same inputs: the first-order model
+  changes the skipped blocks' values only, and the kernel takes the same
+  weights, so the two agree bit for bit;
+* the fused producer step followed by the first-order path;
+* the 720p size (B = 1, H = 40, 21 x 45 x 80, bf16) at tau = 2, the
+  configuration the benchmark times for this mode: masks of every head, O
+  and LSE of sampled query blocks of four heads.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from block_sparse_attention_route_amd import api, synth
+from oracle import attention as orc
+from tests.parity import mask_check, mask_check_topk, output_check, say, to_gpu
+
+pytestmark = pytest.mark.gpu
+
+CASES = [
+    # name, B, H, (T, Hg, Wg), D, tau, topk, tile, scale, seed
+    ("d128_tau1", 1, 2, (3, 10, 13), 128, 1.0, 0, None, 0.0, 31),
+    ("d128_tau0", 2, 1, (2, 16, 20), 128, 0.0, 0, None, 0.0, 32),
+    ("d128_topk3", 1, 3, (4, 9, 15), 128, 0.0, 3, None, 0.0, 33),
+    ("d64_tau2", 2, 2, (3, 12, 12), 64, 2.0, 0, None, 0.0, 34),
+    ("d64_topk2_scale", 1, 2, (2, 14, 11), 64, 0.0, 2, None, 0.09, 35),
+    ("tiles_2x4x8", 1, 2, (4, 8, 17), 128, 0.5, 0, (2, 4, 8), 0.0, 36),
+    ("tiles_4x4x4_topk", 1, 1, (5, 9, 9), 128, 0.0, 4, (4, 4, 4), 0.0, 37),
+    ("one_block", 1, 1, (1, 5, 9), 128, 0.0, 0, None, 0.0, 38),
+]
+
+
+def _run(case, corr):
+    name, B, H, grid, D, tau, topk, tile, scale, seed = case
+    wl = synth.Workload(name, B, H, *grid, D, "bf16", (tau,), True, seed=seed)
+    inp = synth.generate(wl)
+    q, k, v, _, _ = to_gpu(inp)
+    kw = dict(tau=tau, topk=topk, tile=tile, scale=scale)
+    ws = api.sa_pool(q, k, v, grid, correction=corr, **kw)
+    o, lse, kept = api.sa_forward_pooled(q, k, v, grid, workspace=ws, correction=corr, want_kept=True, **kw)
+    return wl, inp, (q, k, v), ws, o, lse, kept
+
+
+@pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
+def test_first_order_parity(case):
+    name, B, H, grid, D, tau, topk, tile, scale, seed = case
+    say(f"case {case}")
+    wl, inp, (q, k, v), ws, o, lse, kept = _run(case, 2)
+    mask, kept_r = api.sa_route(q, k, v, grid, tau=tau, topk=topk, tile=tile, scale=scale)
+    torch.cuda.synchronize()
+    assert torch.equal(kept.cpu(), kept_r.cpu())
+    m = mask.cpu().numpy()
+    order = None if tile is None else orc.tile_order(*grid, tile)
+    sc = scale if scale > 0 else None
+    for b in range(B):
+        for h in range(H):
+            if topk:
+                keep, _, _ = mask_check_topk(inp, b, h, m[b, h], topk, scale=sc, order=order)
+            else:
+                keep, _, _ = mask_check(inp, b, h, m[b, h], tau, scale=sc, order=order)
+            st = output_check(inp, b, h, o, lse, keep, tau, 2, scale=sc, order=order)
+            say(f"  head ({b},{h}): {st}")
+
+
+@pytest.mark.parametrize("case", [CASES[0], CASES[3], CASES[5]], ids=[CASES[i][0] for i in (0, 3, 5)])
+def test_first_order_values(case):
+    """The workspace's first-order values against the oracle, every pair."""
+    name, B, H, grid, D, tau, topk, tile, scale, seed = case
+    say(f"case {case}")
+    wl, inp, (q, k, v), ws, _, _, _ = _run(case, 2)
+    torch.cuda.synchronize()
+    off = api.sa_workspace_bytes(q, k, v, grid, tile=tile, correction=1)
+    Nb = wl.Nb
+    Nbp = (Nb + 63) // 64 * 64
+    n = B * H * Nb * Nbp * D
+    assert ws.numel() - off >= 2 * n
+    vp = ws[off:off + 2 * n].view(torch.bfloat16).view(B, H, Nb, Nbp, D).float().cpu().numpy()
+    assert (vp[:, :, :, Nb:, :] == 0).all(), "padding rows are not zero"
+    s = scale if scale > 0 else 1.0 / math.sqrt(D)
+    order = None if tile is None else np.asarray(orc.tile_order(*grid, tile))
+    ranges = orc.block_ranges(wl.N, 64)
+    for b in range(B):
+        for h in range(H):
+            qh, kh, vh = inp.head64(b, h)
+            if order is not None:
+                qh, kh, vh = qh[order], kh[order], vh[order]
+            ref = np.empty((Nb, Nb, D))
+            mag = np.empty((Nb, Nb, D))
+            for I in range(Nb):
+                qbar = qh[slice(*ranges[I])].mean(axis=0)
+                for J in range(Nb):
+                    kJ, vJ = kh[slice(*ranges[J])], vh[slice(*ranges[J])]
+                    ref[I, J] = orc.first_order_value(qbar, kJ, vJ, s)
+                    # (s / n_J) sum_j |v_j| sum_d |qbar_d| |d_jd|: the scale of the
+                    # rounding inside the first-order term
+                    mag[I, J] = s * (np.abs(kJ - kJ.mean(axis=0)) @ np.abs(qbar)) @ np.abs(vJ) / kJ.shape[0]
+            got = vp[b, h, :, :Nb, :]
+            err = np.abs(got - ref)
+            # the stored value is bf16 (2^-9 relative); inside the first-order term
+            # qbar and each centred score are rounded to bf16 (2^-9 each, relative
+            # to the terms of the sum, hence the absolute-value sum mag); 2x margin
+            bound = 2.0 ** -8 * np.abs(ref) + 2.0 ** -7 * mag + 1e-6
+            say(f"  head ({b},{h}): max err {err.max():.3e}, max |term| sum {mag.max():.3e}, "
+                f"worst err/bound {(err / bound).max():.3f}")
+            assert (err <= bound).all()
+
+
+@pytest.mark.parametrize("case", [CASES[0], CASES[2], CASES[4]], ids=[CASES[i][0] for i in (0, 2, 4)])
+def test_lse_equals_mean_copies(case):
+    say(f"case {case}")
+    _, _, _, _, o2, lse2, _ = _run(case, 2)
+    _, _, _, _, o1, lse1, _ = _run(case, 1)
+    torch.cuda.synchronize()
+    assert torch.equal(lse1, lse2)
+    assert not torch.equal(o1, o2)
+
+
+def test_producer_then_first_order():
+    """sa_qk_prologue with correction 2 leaves the workspace sa_pool would
+    write from its outputs, first-order values included (the producer's own
+    parity is covered with the producer's tests)."""
+    B, H, grid, D = 1, 3, (3, 8, 12), 128
+    N = grid[0] * grid[1] * grid[2]
+    say(f"case producer B={B} H={H} grid={grid}")
+    g = torch.Generator().manual_seed(41)
+    xq = (torch.randn((B, H, N, D), generator=g) * 2).to(torch.bfloat16)
+    xk = (torch.randn((B, H, N, D), generator=g) * 2).to(torch.bfloat16)
+    v = torch.randn((B, H, N, D), generator=g).to(torch.bfloat16)
+    qg = (1 + 0.1 * torch.randn(D, generator=g)).float()
+    kg = (1 + 0.1 * torch.randn(D, generator=g)).float()
+    dev = torch.device("cuda:0")
+    xq, xk, v, qg, kg = (t.to(dev) for t in (xq, xk, v, qg, kg))
+    qo, ko, ws = api.sa_qk_prologue(xq, xk, v, grid, qg, kg, tau=1.0, correction=2)
+    ws2 = api.sa_pool(qo, ko, v, grid, tau=1.0, correction=2)
+    torch.cuda.synchronize()
+    assert torch.equal(ws, ws2)
+
+
+_WL = None
+
+
+def _inputs_720p():
+    global _WL
+    if _WL is None:
+        wl = synth.workload("720p")
+        _WL = (wl, synth.generate(wl))
+    return _WL
+
+
+def test_first_order_720p():
+    from concurrent.futures import ThreadPoolExecutor
+    wl, inp = _inputs_720p()
+    tau = 2.0
+    say(f"case 720p first-order tau={tau}")
+    q, k, v, _, _ = to_gpu(inp)
+    grid = (wl.T, wl.Hg, wl.Wg)
+    ws = api.sa_pool(q, k, v, grid, tau=tau, correction=2)
+    o, lse, kept = api.sa_forward_pooled(q, k, v, grid, tau=tau, correction=2, workspace=ws, want_kept=True)
+    mask, kept_r = api.sa_route(q, k, v, grid, tau=tau)
+    torch.cuda.synchronize()
+    assert torch.equal(kept.cpu(), kept_r.cpu())
+    del ws, q, k, v
+    mask_np = mask.cpu().numpy()
+    del mask
+    heads = [(0, h) for h in range(wl.H)]
+    with ThreadPoolExecutor(max_workers=8) as ex:
+        res = list(ex.map(lambda bh: mask_check(inp, bh[0], bh[1], mask_np[bh], tau), heads))
+    say(f"  masks ok for {len(heads)} heads; density {mask_np.mean():.3f}")
+    rng = np.random.default_rng(11)
+    sample = sorted({(0, 0), (0, wl.H - 1), (0, int(rng.integers(wl.H))), (0, int(rng.integers(wl.H)))})
+    for (b, h) in sample:
+        keep = res[heads.index((b, h))][0]
+        qb = {0, wl.Nb - 1, int(rng.integers(wl.Nb)), int(rng.integers(wl.Nb))}
+        st = output_check(inp, b, h, o, lse, keep, tau, 2, qblocks=qb)
+        say(f"  head ({b},{h}) blocks {sorted(qb)}: {st}")

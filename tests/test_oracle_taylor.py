@@ -195,12 +195,12 @@ def test_taylor_with_tile_order_and_topk():
 
 # ---------------------------------------------------------------- mutants
 MUTANTS = {
-    "sign": ("vbar[t] = vbar[t] + (s * (d @ qbar))", "vbar[t] = vbar[t] - (s * (d @ qbar))"),
-    "no_one_over_n": ("@ v[slice(*ranges[J])] / nJ[t]", "@ v[slice(*ranges[J])]"),
-    "uncentred_keys": ("d = k[slice(*ranges[J])] - kbar[t]", "d = k[slice(*ranges[J])]"),
-    "no_scale": ("vbar[t] = vbar[t] + (s * (d @ qbar))", "vbar[t] = vbar[t] + ((d @ qbar))"),
-    "first_query_row": ("qbar = q_rows.mean(axis=0)", "qbar = q_rows[0]"),
-    "mean_over_block_size": ("@ v[slice(*ranges[J])] / nJ[t]", "@ v[slice(*ranges[J])] / block"),
+    "sign": ("return vJ.mean(axis=0) + (s * (d @ np", "return vJ.mean(axis=0) - (s * (d @ np"),
+    "no_one_over_n": ("@ vJ / kJ.shape[0]", "@ vJ"),
+    "uncentred_keys": ("d = kJ - kJ.mean(axis=0)", "d = kJ"),
+    "no_scale": ("return vJ.mean(axis=0) + (s * (d @ np", "return vJ.mean(axis=0) + (1 * (d @ np"),
+    "first_query_row": ("qbar = q_rows.mean(axis=0)\n            for t, J", "qbar = q_rows[0]\n            for t, J"),
+    "mean_over_block_size": ("@ vJ / kJ.shape[0]", "@ vJ / 64"),
 }
 
 
