@@ -18,7 +18,10 @@ The fixed_budget list times the same call with routing by a fixed number of
 key blocks per query block (sparsity 0.9 and 0.8 by default) instead of tau;
 the tile_order list times it with blocks formed over 3-D tiles of the token
 grid (4x4x4 and 1x8x8 by default); fused_producer times sa_qk_prologue (norm
-+ rotary + pool of the Q/K projections) in place of the pool.
++ rotary + pool of the Q/K projections) in place of the pool; first_order
+times the call with the first-order correction of the skipped blocks
+(correction = 2: the pool step also writes the per-pair values, the fused
+kernel reads them) and its error against dense attention.
 """
 from __future__ import annotations
 
@@ -142,6 +145,13 @@ def cpu_baseline(inp, wl, tau, o_gpu, budget_s: float):
     }
 
 
+def approx_vs(o_s, l_s, od, lsed):
+    """Sparse output against dense attention on the same inputs."""
+    d = o_s.float() - od.float()
+    return {"o_rel_l2": float(d.norm() / od.float().norm()), "o_max_abs": float(d.abs().max()),
+            "lse_mean_abs": float((l_s - lsed).abs().mean())}
+
+
 def main() -> None:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -158,6 +168,8 @@ def main() -> None:
     ap.add_argument("--budget-steps", type=int, default=5)
     ap.add_argument("--tiles", default="4x4x4,1x8x8",
                     help="3-D tile orders (t x h x w, product 64) to time at the same tau ('' for none)")
+    ap.add_argument("--no-first-order", dest="first_order", action="store_false",
+                    help="skip timing the first-order correction (correction = 2)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run one 1 GiB device-to-device copy (reference for the PMC byte counters)")
     args = ap.parse_args()
@@ -251,6 +263,7 @@ def main() -> None:
 
     # dense path at the same shape (the tau = inf baseline)
     dense = None
+    od = lsed = None
     if args.dense_steps > 0:
         wsd = torch.empty(max(api.sa_dense_workspace_bytes(q, k, v, grid), 1), dtype=torch.uint8, device=dev)
         od = torch.empty_like(o)
@@ -270,16 +283,58 @@ def main() -> None:
         # what the method approximates: the sparse output against dense
         # attention on the same inputs, with the correction as configured and
         # toggled (the error the correction of the skipped blocks removes)
-        def approx(o_s, l_s):
-            d = o_s.float() - od.float()
-            return {"o_rel_l2": float(d.norm() / od.float().norm()), "o_max_abs": float(d.abs().max()),
-                    "lse_mean_abs": float((l_s - lsed).abs().mean())}
         o_t, l_t = api.sa_forward(q, k, v, grid, tau=tau, correction=not correction, workspace=ws,
                                   q_scale=qs, k_scale=ks)[:2]
         torch.cuda.synchronize()
-        dense["approx_vs_dense"] = {"tau": tau, ("correction_on" if correction else "correction_off"): approx(o, lse),
-                                    ("correction_off" if correction else "correction_on"): approx(o_t, l_t)}
-        del wsd, od, lsed, o_t, l_t
+        dense["approx_vs_dense"] = {"tau": tau, ("correction_on" if correction else "correction_off"):
+                                    approx_vs(o, lse, od, lsed),
+                                    ("correction_off" if correction else "correction_on"):
+                                    approx_vs(o_t, l_t, od, lsed)}
+        del wsd, o_t, l_t
+
+    # first-order correction of the skipped blocks (correction = 2) at the
+    # same tau: the pool step also writes one first-order value per (query
+    # block, key block), and the fused kernel's correction tiles read them
+    first_order = None
+    if wl.dtype == "bf16" and args.first_order:
+        wsf = torch.empty(api.sa_workspace_bytes(q, k, v, grid, correction=2), dtype=torch.uint8, device=dev)
+        of, lsef = torch.empty_like(o), torch.empty_like(lse)
+
+        def fstep(ev=None):
+            if ev is not None:
+                ev[0].record()
+            api.sa_pool(q, k, v, grid, tau=tau, correction=2, workspace=wsf)
+            if ev is not None:
+                ev[1].record()
+            api.sa_forward_pooled(q, k, v, grid, tau=tau, correction=2, workspace=wsf, out=of, lse=lsef,
+                                  kept=kept, want_kept=True)
+            if ev is not None:
+                ev[2].record()
+        fstep()
+        torch.cuda.synchronize()
+        assert torch.equal(kept.cpu(), kept_r.cpu()), "fused routing disagrees with sa_route (first order)"
+        fevs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.budget_steps)]
+        for i in range(args.budget_steps):
+            fstep(fevs[i])
+        torch.cuda.synchronize()
+        fpool = float(np.mean([e[0].elapsed_time(e[1]) for e in fevs]))
+        ffused = float(np.mean([e[1].elapsed_time(e[2]) for e in fevs]))
+        bh, nbp = wl.B * wl.H, (wl.Nb + 63) // 64 * 64
+        # values kernel: reads K, V (bf16) and the fp32 means, writes the
+        # bf16 values; 4*64*D flops per (query block, key block) pair
+        vbytes = bh * wl.N * wl.D * 2 * 2 + 3 * bh * wl.Nb * wl.D * 4 + bh * wl.Nb * nbp * wl.D * 2
+        vflops = 4.0 * 64 * wl.D * bh * wl.Nb * wl.Nb
+        vms = fpool - pool_avg
+        first_order = {"tau": tau, "ms": fpool + ffused, "pool_and_values_ms": fpool,
+                       "values_ms_by_difference": vms, "fused_kernel_ms": ffused,
+                       "values_bytes": vbytes, "values_gbs": vbytes / (vms * 1e-3) / 1e9,
+                       "values_tflops": vflops / (vms * 1e-3) / 1e12,
+                       "workspace_gib": wsf.numel() / 2 ** 30,
+                       "time_vs_mean_copies": (fpool + ffused) / ms_step,
+                       "approx_vs_dense": approx_vs(of, lsef, od, lsed) if od is not None else None}
+        log(f"first-order correction: pool+values {fpool:.2f} ms, fused {ffused:.2f} ms")
+        del wsf, of, lsef
+    del od, lsed
 
     # fixed-budget routing (topk blocks per query block) at the same shape
     budgets = []
@@ -440,6 +495,7 @@ def main() -> None:
         "fixed_budget": budgets,
         "tile_order": tiled,
         "fused_producer": producer,
+        "first_order": first_order,
         "cpu_baseline": cpu,
         "kernel_src": kernel_source_hash(),
     }

@@ -80,7 +80,6 @@ struct AttnArgs {
   const uint16_t* vt16;
   TileMap tm;            // position -> token order (on == 0: raster)
   const uint16_t* kpos16;  // K in position order when tm.on (bf16 K)
-  const uint16_t* vprime;  // correction mode 2: first-order values, else null
   void* o;
   float* lse;
   int32_t* kept;
@@ -91,6 +90,7 @@ struct AttnArgs {
   int topk;              // > 0: fixed budget of key blocks per query block
   int correction;
   bool sparse;           // false: dense attention over all blocks
+  const uint16_t* vprime;  // correction mode 2: first-order values, else null
 };
 
 hipError_t launch_pool(const PoolArgs& a, hipStream_t st);

@@ -16,24 +16,31 @@
 // bf16, [BH][Nb][Nbp][D], rows J >= Nb zero; the fused attention kernel then
 // reads rows [I][64c, 64c + 64) as the values of correction tile c.
 //
-// Workgroup: one head, 128 query blocks (four waves of 32, one per lane
-// column) and one chunk of 64 key blocks.  For each key block J it computes,
-// like an attention tile with the block means as queries,
-//   S^T = K_J Qbar^T       v_mfma_f32_32x32x16_bf16 on bf16(qbar_I)
-//   S~  = S^T - r_IJ       r_IJ = bf16(qbar_I) . kbar_J in fp32: centred
-//                          scores, whose sum over the block vanishes; keys
-//                          past the end of the sequence give 0
-//   U^T = V_J^T bf16(S~)   the same MFMA, V_J^T from the regrouped V
-// and writes vbar_J + (s / n_J) U.  The K and V^T tiles of the next key block
-// are fetched into registers while the current one is used and handed over
-// through a second LDS buffer, so one barrier per key block suffices.
+// Workgroup: one head, 256 query blocks (eight waves of 32, one per lane
+// column) and one chunk of 64 key blocks.  With c = s / 64 and qc_I =
+// bf16(c qbar_I), for each key block J it computes, like an attention tile
+// with the scaled block means as queries,
+//   S~^T = K_J qc^T - r_IJ  v_mfma_f32_32x32x16_bf16, the accumulator starting
+//                           at -r_IJ = -qc_I . kbar_J (kbar_J split into two
+//                           bf16 halves, v_dot2_f32_bf16): centred scores,
+//                           whose sum over the block vanishes; keys past the
+//                           end of the sequence give 0, and the ragged last
+//                           block scales them by 64 / n_J
+//   V'^T = vbar_J + V_J^T bf16(S~^T)   the same MFMA, the accumulator starting
+//                           at vbar_J, V_J^T from the regrouped V
+// and writes V' in bf16.  The K and V^T tiles of the next key block are
+// fetched into registers while the current one is used and handed over
+// through a second LDS buffer, so one barrier per key block suffices.  Each
+// wave turns its 32 output rows around in LDS and writes them as whole rows,
+// 16 bytes per lane (written straight from the MFMA layout, every store
+// would touch 32 rows).
 #include "sa_device.h"
 #include "sa_kernels.h"
 
 namespace sa {
 namespace {
 
-constexpr int kTyWaves = 4;             // waves per workgroup
+constexpr int kTyWaves = 8;             // waves per workgroup
 constexpr int kTyRows = 32 * kTyWaves;  // query blocks per workgroup
 constexpr int kTyThreads = 64 * kTyWaves;
 
@@ -47,16 +54,20 @@ struct TyCfg {
   static constexpr int VTILE = D * 128;       // V^T tile: D rows of 64 bf16 keys
   static constexpr int KLD = KTILE / 16 / kTyThreads;  // 16-byte copies per thread
   static constexpr int VLD = VTILE / 16 / kTyThreads;
+  static constexpr int OST = 32 * KROW / 16 / 64;   // 16-byte output stores per lane: 32 rows of D bf16
 };
 
 template <int D>
-__global__ __launch_bounds__(kTyThreads, 2) void taylor_kernel(TaylorArgs a) {
+__global__ __launch_bounds__(kTyThreads, 1) void taylor_kernel(TaylorArgs a) {
   using C = TyCfg<D>;
   static_assert(C::KLD >= 1 && C::VLD >= 1, "tile copies per thread");
   __shared__ __attribute__((aligned(16))) uint8_t kt[2][C::KTILE];
   __shared__ __attribute__((aligned(16))) uint8_t vt[2][C::VTILE];
-  __shared__ __attribute__((aligned(16))) float kb[2][D];
+  __shared__ __attribute__((aligned(16))) __bf16 kbh[2][2][D];   // kbar_J: bf16 high and low parts
   __shared__ __attribute__((aligned(16))) float vb[2][D];
+  // per wave: its 32 output rows of the current key block, 16-byte chunks
+  // XOR-swizzled by row, so that the rows go out as whole rows
+  __shared__ __attribute__((aligned(16))) uint8_t ost[kTyWaves][32 * C::KROW];
 
   const int N = a.N, Nb = a.Nb, Nbp = a.Nbp;
   const int nit = (Nb + kTyRows - 1) / kTyRows;
@@ -74,7 +85,8 @@ __global__ __launch_bounds__(kTyThreads, 2) void taylor_kernel(TaylorArgs a) {
   const int Jend = min(J0 + 64, Nb);                  // key blocks with data
   const int ntail = N - (Nb - 1) * kBlock;
 
-  // bf16(qbar_I): the B operand of S^T
+  // qc_I = bf16(s / 64 * qbar_I): the B operand of S~^T
+  const float c64 = a.scale / (float)kBlock;
   bf16x8 qr[C::KS];
 #pragma unroll
   for (int ks = 0; ks < C::KS; ++ks) {
@@ -85,8 +97,8 @@ __global__ __launch_bounds__(kTyThreads, 2) void taylor_kernel(TaylorArgs a) {
       const f32x4 hi = *reinterpret_cast<const f32x4*>(src + 4);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        x[e] = static_cast<__bf16>(lo[e]);
-        x[e + 4] = static_cast<__bf16>(hi[e]);
+        x[e] = static_cast<__bf16>(c64 * lo[e]);
+        x[e + 4] = static_cast<__bf16>(c64 * hi[e]);
       }
     }
     qr[ks] = x;
@@ -126,9 +138,20 @@ __global__ __launch_bounds__(kTyThreads, 2) void taylor_kernel(TaylorArgs a) {
       const int P = tid + kTyThreads * i;
       *reinterpret_cast<u32x4*>(&vt[buf][16 * P]) = vr[i];
     }
-    if (tid < D / 2) {
-      float* m = (tid < D / 4 ? kb[buf] : vb[buf]) + 4 * (tid % (D / 4));
-      *reinterpret_cast<u32x4*>(m) = mr;
+    if (tid < D / 4) {
+      // kbar = hi + lo with both parts in bf16 (relative error 2^-16)
+      typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+      bf16x4 hi, lo;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float x = __uint_as_float(mr[e]);
+        hi[e] = static_cast<__bf16>(x);
+        lo[e] = static_cast<__bf16>(x - static_cast<float>(hi[e]));
+      }
+      *reinterpret_cast<bf16x4*>(&kbh[buf][0][4 * tid]) = hi;
+      *reinterpret_cast<bf16x4*>(&kbh[buf][1][4 * tid]) = lo;
+    } else if (tid < D / 2) {
+      *reinterpret_cast<u32x4*>(&vb[buf][4 * (tid - D / 4)]) = mr;
     }
   };
 
@@ -138,35 +161,48 @@ __global__ __launch_bounds__(kTyThreads, 2) void taylor_kernel(TaylorArgs a) {
   }
   __syncthreads();
 
-  const float s = a.scale;
   for (int j = 0; j < 64; ++j) {
     const int J = J0 + j, buf = j & 1;
     const bool more = J + 1 < Jend;
     if (more) fetch(J + 1);
-    uint16_t* orow = a.vprime + (((size_t)bh * Nb + (ivalid ? I : 0)) * Nbp + J) * D;
+    // output rows of this wave: 16 bytes per lane and store, whole rows
+    auto store_rows = [&](auto chunk_of) __attribute__((always_inline)) {
+#pragma unroll
+      for (int i = 0; i < C::OST; ++i) {
+        const int q = 64 * i + lane, row = q / C::CPR, c = q % C::CPR;
+        const int Ir = kTyRows * itile + 32 * wave + row;
+        const u32x4 x = chunk_of(row, c);
+        if (Ir < Nb)
+          *reinterpret_cast<u32x4*>(a.vprime + (((size_t)bh * Nb + Ir) * Nbp + J) * D + 8 * c) = x;
+      }
+    };
     if (J < Jend) {
       const uint8_t* Kb = kt[buf];
       const uint8_t* Vb = vt[buf];
-      // r_IJ = bf16(qbar_I) . kbar_J: this lane's half of d, plus lane^32's
+      // r_IJ = qc_I . kbar_J: this lane's half of d, plus lane^32's
+      typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
       float rp = 0.f;
 #pragma unroll
       for (int ks = 0; ks < C::KS; ++ks) {
-        const f32x4 lo = *reinterpret_cast<const f32x4*>(&kb[buf][16 * ks + 8 * h]);
-        const f32x4 hi = *reinterpret_cast<const f32x4*>(&kb[buf][16 * ks + 8 * h + 4]);
+        const bf16x8 kh = *reinterpret_cast<const bf16x8*>(&kbh[buf][0][16 * ks + 8 * h]);
+        const bf16x8 kl = *reinterpret_cast<const bf16x8*>(&kbh[buf][1][16 * ks + 8 * h]);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          rp = fmaf(static_cast<float>(qr[ks][e]), lo[e], rp);
-          rp = fmaf(static_cast<float>(qr[ks][e + 4]), hi[e], rp);
+        for (int e = 0; e < 8; e += 2) {
+          const bf16x2 qp = {qr[ks][e], qr[ks][e + 1]};
+          const bf16x2 hp = {kh[e], kh[e + 1]};
+          const bf16x2 lp = {kl[e], kl[e + 1]};
+          rp = __builtin_amdgcn_fdot2_f32_bf16(qp, hp, rp, false);
+          rp = __builtin_amdgcn_fdot2_f32_bf16(qp, lp, rp, false);
         }
       }
       const float r = rp + __shfl_xor(rp, 32);
 
-      // S^T = K_J Qbar^T
+      // S~^T = K_J qc^T - r_IJ
       f32x16 sc[2];
 #pragma unroll
       for (int k2 = 0; k2 < 2; ++k2)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) sc[k2][e] = 0.f;
+        for (int e = 0; e < 16; ++e) sc[k2][e] = -r;
 #pragma unroll
       for (int ks = 0; ks < C::KS; ++ks) {
 #pragma unroll
@@ -176,52 +212,59 @@ __global__ __launch_bounds__(kTyThreads, 2) void taylor_kernel(TaylorArgs a) {
           sc[k2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qr[ks], sc[k2], 0, 0, 0);
         }
       }
-      // centred scores in bf16, the B operand of U^T; keys past the sequence end give 0
-      const int nJ = (J == Nb - 1) ? ntail : kBlock;
+      // centred scores in bf16, the B operand of V'^T; the ragged last block:
+      // keys past the sequence end give 0, the others are scaled to s / n_J
       bf16x8 pb[4];
+      if (J == Nb - 1 && ntail < kBlock) {
+        const float f = (float)kBlock / (float)ntail;
 #pragma unroll
-      for (int k2 = 0; k2 < 2; ++k2)
+        for (int k2 = 0; k2 < 2; ++k2)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const bool live = 32 * k2 + key_of(e, h) < nJ;
-          pb[2 * k2 + (e >> 3)][e & 7] = static_cast<__bf16>(live ? sc[k2][e] - r : 0.f);
-        }
+          for (int e = 0; e < 16; ++e) {
+            const bool live = 32 * k2 + key_of(e, h) < ntail;
+            pb[2 * k2 + (e >> 3)][e & 7] = static_cast<__bf16>(live ? sc[k2][e] * f : 0.f);
+          }
+      } else {
+#pragma unroll
+        for (int k2 = 0; k2 < 2; ++k2)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) pb[2 * k2 + (e >> 3)][e & 7] = static_cast<__bf16>(sc[k2][e]);
+      }
 
-      // U^T = V_J^T S~^T, then vbar_J + (s / n_J) U
-      const float coef = s / (float)nJ;
+      // V'^T = vbar_J + V_J^T S~^T
 #pragma unroll
       for (int dt = 0; dt < C::DT; ++dt) {
         const int vrow = 32 * dt + l32;
         f32x16 acc;
 #pragma unroll
-        for (int e = 0; e < 16; ++e) acc[e] = 0.f;
+        for (int g = 0; g < 4; ++g) {
+          const f32x4 vm = *reinterpret_cast<const f32x4*>(&vb[buf][32 * dt + 8 * g + 4 * h]);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc[4 * g + e] = vm[e];
+        }
 #pragma unroll
         for (int k4 = 0; k4 < 4; ++k4) {
           const bf16x8 va = *reinterpret_cast<const bf16x8*>(Vb + vrow * 128 + swz<8>(vrow, 2 * k4 + h) * 16);
           acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[k4], acc, 0, 0, 0);
         }
-        if (ivalid) {
+        // row l32 of the wave's staging area, d = 32 dt + 8 g + 4 h .. + 3
 #pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            const int d = 32 * dt + 8 * g + 4 * h;
-            const f32x4 vm = *reinterpret_cast<const f32x4*>(&vb[buf][d]);
-            u32x2 w;
-            w[0] = (uint32_t)f32_to_bf16_bits(fmaf(coef, acc[4 * g + 0], vm[0])) |
-                   ((uint32_t)f32_to_bf16_bits(fmaf(coef, acc[4 * g + 1], vm[1])) << 16);
-            w[1] = (uint32_t)f32_to_bf16_bits(fmaf(coef, acc[4 * g + 2], vm[2])) |
-                   ((uint32_t)f32_to_bf16_bits(fmaf(coef, acc[4 * g + 3], vm[3])) << 16);
-            *reinterpret_cast<u32x2*>(orow + d) = w;
-          }
+        for (int g = 0; g < 4; ++g) {
+          u32x2 w;
+          w[0] = (uint32_t)f32_to_bf16_bits(acc[4 * g + 0]) | ((uint32_t)f32_to_bf16_bits(acc[4 * g + 1]) << 16);
+          w[1] = (uint32_t)f32_to_bf16_bits(acc[4 * g + 2]) | ((uint32_t)f32_to_bf16_bits(acc[4 * g + 3]) << 16);
+          const int c = 4 * dt + g;
+          *reinterpret_cast<u32x2*>(&ost[wave][l32 * C::KROW + (c ^ (l32 & (C::CPR - 1))) * 16 + 8 * h]) = w;
         }
       }
-    } else if (ivalid) {
+      // the wave's own staging area: no barrier, LDS accesses of a wave are ordered
+      store_rows([&](int row, int c) {
+        return *reinterpret_cast<const u32x4*>(&ost[wave][row * C::KROW + (c ^ (row & (C::CPR - 1))) * 16]);
+      });
+    } else {
       // key blocks J >= Nb: zero rows (the attention kernel masks them, but
       // reads them as MFMA operands)
-      const u32x2 z = {0u, 0u};
-#pragma unroll
-      for (int dt = 0; dt < C::DT; ++dt)
-#pragma unroll
-        for (int g = 0; g < 4; ++g) *reinterpret_cast<u32x2*>(orow + 32 * dt + 8 * g + 4 * h) = z;
+      store_rows([](int, int) { return u32x4{0u, 0u, 0u, 0u}; });
     }
     if (more) stash(buf ^ 1);
     __syncthreads();
