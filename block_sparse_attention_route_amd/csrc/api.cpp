@@ -83,6 +83,9 @@ sa_status check_shape_inputs(const sa_shape* sh, const sa_inputs* in, Req* r, bo
   r->dense = dense;
   r->tm = sa::make_tile_map(sh->T, sh->Hg, sh->Wg, 0, 0, 0);
   if (r->BH > (int64_t)1 << 24) return fail(SA_ERR_SHAPE, "B*H too large");
+  // every launch's grid has at most B*H*Nb workgroups: keep it a positive int
+  if (r->BH * r->Nb > (int64_t)INT32_MAX)
+    return fail(SA_ERR_SHAPE, "B*H*Nb (%lld) exceeds 2^31 - 1", (long long)(r->BH * r->Nb));
   r->ws = sa::ws_layout(r->BH, r->N, r->D, v == SA_BF16, dense);
   if (!ptrs) return SA_OK;  // sizing only: data pointers are not needed
   if (!fp8 && (in->q_scale || in->k_scale))

@@ -62,7 +62,7 @@ extern "C" {
 typedef enum sa_status {
   SA_OK = 0,
   SA_ERR_NULL = 1,        /* a required pointer is NULL */
-  SA_ERR_SHAPE = 2,       /* bad B/H/N/D, N != T*Hg*Wg, or N > SA_MAX_N */
+  SA_ERR_SHAPE = 2,       /* bad B/H/N/D, N != T*Hg*Wg, N > SA_MAX_N, or B*H*Nb > 2^31 - 1 */
   SA_ERR_PARAM = 3,       /* block != 64, tau < 0 or NaN, topk < 0, bad correction flag, bad scale */
   SA_ERR_DTYPE = 4,       /* unsupported (qk_dtype, v_dtype) pair or scales given/missing */
   SA_ERR_ALIGN = 5,       /* pointer misaligned */

@@ -83,6 +83,7 @@ def test_workspace_bytes_layout(lib):
     (dict(N=100), "SA_ERR_SHAPE"),               # N != T*Hg*Wg
     (dict(T=65, Hg=64, Wg=64), "SA_ERR_SHAPE"),  # N > SA_MAX_N
     (dict(B=-1), "SA_ERR_SHAPE"),
+    (dict(B=1, H=1 << 24, T=2, Hg=64, Wg=64), "SA_ERR_SHAPE"),   # B*H*Nb = 2^31 workgroups
 ])
 def test_bad_shapes(lib, kw, code):
     sh = _shape(**kw)
