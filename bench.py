@@ -332,8 +332,18 @@ def main() -> None:
                        "workspace_gib": wsf.numel() / 2 ** 30,
                        "time_vs_mean_copies": (fpool + ffused) / ms_step,
                        "approx_vs_dense": approx_vs(of, lsef, od, lsed) if od is not None else None}
+        del wsf
+        if od is not None:
+            # with blocks over 4x4x4 tiles of the grid the keys of a block lie
+            # closer together, and the first-order term matters more
+            tiled_err = {"tile": [4, 4, 4], "tau": tau}
+            for name, corr in (("mean_copies", 1), ("first_order", 2)):
+                api.sa_forward(q, k, v, grid, tau=tau, correction=corr, tile=(4, 4, 4), out=of, lse=lsef)
+                torch.cuda.synchronize()
+                tiled_err[name] = approx_vs(of, lsef, od, lsed)
+            first_order["approx_vs_dense_tiled"] = tiled_err
         log(f"first-order correction: pool+values {fpool:.2f} ms, fused {ffused:.2f} ms")
-        del wsf, of, lsef
+        del of, lsef
     del od, lsed
 
     # fixed-budget routing (topk blocks per query block) at the same shape
