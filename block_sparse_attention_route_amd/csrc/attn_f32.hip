@@ -9,7 +9,9 @@
 //
 // One wave per query block; lane i owns query row 64*I + i, holds q_i and its
 // output accumulator in registers, and reads keys and values broadcast from
-// LDS, 16 at a time, with natural exp and one rescale per group.
+// LDS, 16 at a time, with natural exp and one rescale per group.  With the
+// first-order correction a skipped block's value is its first-order value for
+// this query block instead of its mean.
 #include "sa_device.h"
 #include "sa_kernels.h"
 
@@ -101,7 +103,8 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(AttnArgs a) {
   const float* kin = reinterpret_cast<const float*>(a.k) + (size_t)bh * N * D;
   const float* vin = reinterpret_cast<const float*>(a.v) + (size_t)bh * N * D;
 
-  // correction: skipped blocks as n_J copies of (kbar_J, vbar_J), 64 at a time
+  // correction: skipped blocks as n_J copies of (kbar_J, vbar_J) -- or of
+  // (kbar_J, V'[I][J]) with first-order values -- 64 at a time
   if (SPARSE && a.correction) {
     const int ntail = N - (Nb - 1) * kBlock;
     for (int J0 = 0; J0 < Nb; J0 += kBlock) {
@@ -109,7 +112,8 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(AttnArgs a) {
       for (int J = J0; J < min(Nb, J0 + kBlock); ++J) {
         if (flags[J] & 1) continue;
         const float* kb = a.kbar + ((size_t)bh * Nb + J) * D;
-        const float* vb = a.vbar + ((size_t)bh * Nb + J) * D;
+        const float* vb = a.vprime32 ? a.vprime32 + (((size_t)bh * Nb + I) * Nb + J) * D
+                                     : a.vbar + ((size_t)bh * Nb + J) * D;
         for (int d = lane; d < D; d += 64) {
           kt[cnt * D + d] = kb[d];
           vt[cnt * D + d] = vb[d];

@@ -44,16 +44,21 @@ struct PoolArgs {
   ProArgs pro;           // producer step fused in front (pro.on)
 };
 
-// First-order values of the skipped blocks (correction mode 2, bf16 only).
+// First-order values of the skipped blocks (correction mode 2): the bf16
+// path (vprime) or the float32 path (vprime32), whichever is set.
 struct TaylorArgs {
-  const uint16_t* k;     // [BH][N][D] bf16 K in position order (the caller's K, or kpos16)
+  const uint16_t* k;     // bf16: [BH][N][D] K in position order (the caller's K, or kpos16)
   const float* qbar;     // [BH][Nb][D]
   const float* kbar;
   const float* vbar;
-  const uint16_t* vt16;  // [BH][Nb][D][64]
-  uint16_t* vprime;      // [BH][Nb][Nbp][D]
+  const uint16_t* vt16;  // bf16: [BH][Nb][D][64]
+  uint16_t* vprime;      // bf16: [BH][Nb][Nbp][D]
   int BH, N, Nb, Nbp, D;
   float scale;           // softmax scale s
+  const float* kf;       // float32: [BH][N][D] K and V in token order, read through tm
+  const float* vf;
+  TileMap tm;
+  float* vprime32;       // float32: [BH][Nb][Nb][D]
 };
 
 struct RouteArgs {
@@ -91,6 +96,7 @@ struct AttnArgs {
   int correction;
   bool sparse;           // false: dense attention over all blocks
   const uint16_t* vprime;  // correction mode 2: first-order values, else null
+  const float* vprime32;   // the same for the float32 path
 };
 
 hipError_t launch_pool(const PoolArgs& a, hipStream_t st);

@@ -14,6 +14,7 @@
 //   vprime  bf16  [BH][Nb][Nbp][D]    first-order values of the skipped blocks,
 //                                     per query block I and key block J, rows
 //                                     J >= Nb zero; only with correction mode 2
+//                                     (fp32 inputs: float [BH][Nb][Nb][D])
 //
 // The dense path uses only vt16.  Blocks are formed over positions: position
 // i is token i in the raster order, or token_of(i) in the 3-D tile order.
@@ -115,7 +116,8 @@ __host__ __device__ inline WsLayout ws_layout(int64_t BH, int64_t N, int64_t D, 
   }
   if (v_bf16) L.vt16 = take((size_t)(BH * Nb * D * kBlock) * 2);
   if (tiled && v_bf16 && !dense_only) L.kpos16 = take((size_t)(BH * N * D) * 2);
-  if (first_order && v_bf16 && !dense_only) L.vprime = take((size_t)BH * Nb * Nbp * D * 2);
+  if (first_order && !dense_only)
+    L.vprime = v_bf16 ? take((size_t)BH * Nb * Nbp * D * 2) : take((size_t)BH * Nb * Nb * D * 4);
   L.total = off;
   return L;
 }

@@ -271,6 +271,52 @@ __global__ __launch_bounds__(kTyThreads, 1) void taylor_kernel(TaylorArgs a) {
   }
 }
 
+// Float32 values for the float32 path (correctness rather than speed): one
+// wave per (query block, head); per key block J, lane j forms the centred
+// score qbar_I . (k_j - kbar_J) of key j, then lane d sums the keys' values
+// in column d.  Rows are read through the position -> token map.  Only
+// J < Nb is written ([BH][Nb][Nb][D]).
+template <int D>
+__global__ __launch_bounds__(64) void taylor_f32_kernel(TaylorArgs a) {
+  const int N = a.N, Nb = a.Nb;
+  const int bh = blockIdx.y, I = blockIdx.x, lane = threadIdx.x;
+  __shared__ float qb[D];
+  __shared__ float t[kBlock];
+  __shared__ int tok[kBlock];
+  for (int d = lane; d < D; d += 64) qb[d] = a.qbar[((size_t)bh * Nb + I) * D + d];
+  const float* kin = a.kf + (size_t)bh * N * D;
+  const float* vin = a.vf + (size_t)bh * N * D;
+  const int ntail = N - (Nb - 1) * kBlock;
+  for (int J = 0; J < Nb; ++J) {
+    const int n = (J == Nb - 1) ? ntail : kBlock;
+    tok[lane] = lane < n ? token_of(a.tm, J * kBlock + lane) : 0;
+    __syncthreads();
+    const float* kb = a.kbar + ((size_t)bh * Nb + J) * D;
+    float tj = 0.f;
+    if (lane < n) {
+      const float* kr = kin + (size_t)tok[lane] * D;
+      for (int d = 0; d < D; ++d) tj = fmaf(qb[d], kr[d] - kb[d], tj);
+    }
+    t[lane] = tj;
+    __syncthreads();
+    const float c = a.scale / (float)n;
+    const float* vb = a.vbar + ((size_t)bh * Nb + J) * D;
+    float* out = a.vprime32 + (((size_t)bh * Nb + I) * Nb + J) * D;
+    for (int d = lane; d < D; d += 64) {
+      float u = 0.f;
+      for (int j = 0; j < n; ++j) u = fmaf(t[j], vin[(size_t)tok[j] * D + d], u);
+      out[d] = fmaf(c, u, vb[d]);
+    }
+    __syncthreads();
+  }
+}
+
+template <int D>
+hipError_t launch_f32(const TaylorArgs& a, hipStream_t st) {
+  hipLaunchKernelGGL(taylor_f32_kernel<D>, dim3(a.Nb, a.BH), dim3(64), 0, st, a);
+  return hipGetLastError();
+}
+
 template <int D>
 hipError_t launch_d(const TaylorArgs& a, hipStream_t st) {
   const int nit = (a.Nb + kTyRows - 1) / kTyRows;
@@ -283,6 +329,7 @@ hipError_t launch_d(const TaylorArgs& a, hipStream_t st) {
 
 hipError_t launch_taylor(const TaylorArgs& a, hipStream_t st) {
   if (a.BH == 0 || a.Nb == 0) return hipSuccess;
+  if (a.vprime32) return a.D == 64 ? launch_f32<64>(a, st) : launch_f32<128>(a, st);
   return a.D == 64 ? launch_d<64>(a, st) : launch_d<128>(a, st);
 }
 

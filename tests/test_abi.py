@@ -174,12 +174,8 @@ def test_tile_order_with_fp8_is_unsupported(lib):
     assert api.status_name(st) == "SA_ERR_UNSUPPORTED"
 
 
-@pytest.mark.parametrize("qk,v,scales", [
-    (api.SA_FP8_E4M3, api.SA_BF16, True),
-    (api.SA_F32, api.SA_F32, False),
-])
-def test_first_order_correction_needs_bf16(lib, qk, v, scales):
-    inp = _inputs(qk=qk, v=v, qs=FAKE if scales else None, ks=FAKE if scales else None)
+def test_first_order_correction_with_fp8_is_unsupported(lib):
+    inp = _inputs(qk=api.SA_FP8_E4M3, v=api.SA_BF16, qs=FAKE, ks=FAKE)
     assert api.status_name(_fwd(lib, _shape(), _params(corr=2), inp)) == "SA_ERR_UNSUPPORTED"
 
 
@@ -192,6 +188,11 @@ def test_first_order_workspace_holds_values_per_block_pair(lib):
     n3 = lib.sa_workspace_bytes(ctypes.byref(sh), ctypes.byref(_params(corr=2, tile=(1, 8, 8))),
                                 ctypes.byref(_inputs()))
     assert n3 - n2 == (6 * 130 * 128 * 2 + 255) // 256 * 256
+    # fp32: float values, [BH][Nb][Nb][D]
+    f32 = _inputs(api.SA_F32, api.SA_F32)
+    m1 = lib.sa_workspace_bytes(ctypes.byref(sh), ctypes.byref(_params()), ctypes.byref(f32))
+    m2 = lib.sa_workspace_bytes(ctypes.byref(sh), ctypes.byref(_params(corr=2)), ctypes.byref(f32))
+    assert m2 - m1 == (6 * 3 * 3 * 128 * 4 + 255) // 256 * 256
 
 
 def test_tiled_workspace_holds_k_in_tile_order(lib):

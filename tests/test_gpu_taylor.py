@@ -3,8 +3,9 @@ oracle.
 
 * seeded cases spanning several tiles and a ragged tail: D = 128 and 64,
   threshold and fixed budget, raster and 3-D tile order, batch and heads
-  above one, explicit scale: masks and every row's O and LSE against the
-  oracle's first-order model;
+  above one, explicit scale, bf16 and float32 inputs: masks and every row's O
+  and LSE against the oracle's first-order model (float32 at its 1e-5
+  bounds);
 * the first-order values themselves (the section sa_pool appends to the
   workspace) against oracle.first_order_value for every (query block, key
   block) pair of a case, padding rows zero;
@@ -38,12 +39,16 @@ CASES = [
     ("tiles_2x4x8", 1, 2, (4, 8, 17), 128, 0.5, 0, (2, 4, 8), 0.0, 36),
     ("tiles_4x4x4_topk", 1, 1, (5, 9, 9), 128, 0.0, 4, (4, 4, 4), 0.0, 37),
     ("one_block", 1, 1, (1, 5, 9), 128, 0.0, 0, None, 0.0, 38),
+    # float32 inputs: the float32 path, at its tighter tolerances
+    ("f32_d64_tau1", 1, 2, (2, 12, 13), 64, 1.0, 0, None, 0.0, 39, "f32"),
+    ("f32_d128_topk3_tiles", 2, 1, (4, 8, 12), 128, 0.0, 3, (2, 4, 8), 0.0, 40, "f32"),
 ]
 
 
 def _run(case, corr):
-    name, B, H, grid, D, tau, topk, tile, scale, seed = case
-    wl = synth.Workload(name, B, H, *grid, D, "bf16", (tau,), True, seed=seed)
+    name, B, H, grid, D, tau, topk, tile, scale, seed = case[:10]
+    dtype = case[10] if len(case) > 10 else "bf16"
+    wl = synth.Workload(name, B, H, *grid, D, dtype, (tau,), True, seed=seed)
     inp = synth.generate(wl)
     q, k, v, _, _ = to_gpu(inp)
     kw = dict(tau=tau, topk=topk, tile=tile, scale=scale)
@@ -54,7 +59,7 @@ def _run(case, corr):
 
 @pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
 def test_first_order_parity(case):
-    name, B, H, grid, D, tau, topk, tile, scale, seed = case
+    name, B, H, grid, D, tau, topk, tile, scale, seed = case[:10]
     say(f"case {case}")
     wl, inp, (q, k, v), ws, o, lse, kept = _run(case, 2)
     mask, kept_r = api.sa_route(q, k, v, grid, tau=tau, topk=topk, tile=tile, scale=scale)
@@ -76,7 +81,7 @@ def test_first_order_parity(case):
 @pytest.mark.parametrize("case", [CASES[0], CASES[3], CASES[5]], ids=[CASES[i][0] for i in (0, 3, 5)])
 def test_first_order_values(case):
     """The workspace's first-order values against the oracle, every pair."""
-    name, B, H, grid, D, tau, topk, tile, scale, seed = case
+    name, B, H, grid, D, tau, topk, tile, scale, seed = case[:10]
     say(f"case {case}")
     wl, inp, (q, k, v), ws, _, _, _ = _run(case, 2)
     torch.cuda.synchronize()
@@ -114,6 +119,40 @@ def test_first_order_values(case):
             say(f"  head ({b},{h}): max err {err.max():.3e}, max |term| sum {mag.max():.3e}, "
                 f"worst err/bound {(err / bound).max():.3f}")
             assert (err <= bound).all()
+
+
+@pytest.mark.parametrize("case", [c for c in CASES if len(c) > 10], ids=[c[0] for c in CASES if len(c) > 10])
+def test_first_order_values_f32(case):
+    """Float32 path: its values section ([BH][Nb][Nb][D] float) against the
+    oracle, every pair, at float32 rounding."""
+    name, B, H, grid, D, tau, topk, tile, scale, seed = case[:10]
+    say(f"case {case}")
+    wl, inp, (q, k, v), ws, _, _, _ = _run(case, 2)
+    torch.cuda.synchronize()
+    off = api.sa_workspace_bytes(q, k, v, grid, tile=tile, correction=1)
+    Nb = wl.Nb
+    n = B * H * Nb * Nb * D
+    vp = ws[off:off + 4 * n].view(torch.float32).view(B, H, Nb, Nb, D).cpu().numpy().astype(np.float64)
+    s = scale if scale > 0 else 1.0 / math.sqrt(D)
+    order = None if tile is None else np.asarray(orc.tile_order(*grid, tile))
+    ranges = orc.block_ranges(wl.N, 64)
+    for b in range(B):
+        for h in range(H):
+            qh, kh, vh = inp.head64(b, h)
+            if order is not None:
+                qh, kh, vh = qh[order], kh[order], vh[order]
+            worst = 0.0
+            for I in range(Nb):
+                qbar = qh[slice(*ranges[I])].mean(axis=0)
+                for J in range(Nb):
+                    kJ, vJ = kh[slice(*ranges[J])], vh[slice(*ranges[J])]
+                    ref = orc.first_order_value(qbar, kJ, vJ, s)
+                    mag = s * (np.abs(kJ - kJ.mean(axis=0)) @ np.abs(qbar)) @ np.abs(vJ) / kJ.shape[0]
+                    bound = 1e-6 * (np.abs(ref) + mag) + 1e-7
+                    err = np.abs(vp[b, h, I, J] - ref)
+                    worst = max(worst, float((err / bound).max()))
+                    assert (err <= bound).all(), (b, h, I, J, float(err.max()))
+            say(f"  head ({b},{h}): worst err/bound {worst:.3f}")
 
 
 @pytest.mark.parametrize("case", [CASES[0], CASES[2], CASES[4]], ids=[CASES[i][0] for i in (0, 2, 4)])
