@@ -108,8 +108,6 @@ sa_status check_params(const sa_params* p, Req* r) {
   if (p->topk == 0 && (std::isnan(p->tau) || p->tau < 0.f))
     return fail(SA_ERR_PARAM, "tau must be >= 0 or +inf");
   if (p->correction < 0 || p->correction > 2) return fail(SA_ERR_PARAM, "correction must be 0, 1 or 2");
-  if (p->correction == 2 && r->qk == SA_FP8_E4M3)
-    return fail(SA_ERR_UNSUPPORTED, "the first-order correction needs bf16 or fp32 Q/K/V");
   if (!std::isfinite(p->scale)) return fail(SA_ERR_PARAM, "scale must be finite");
   const int tt = p->tile_t, th = p->tile_h, tw = p->tile_w;
   if (tt != 0 || th != 0 || tw != 0) {
@@ -238,7 +236,8 @@ sa_status hip_status(hipError_t e, const char* what) {
 // pooled means in the workspace and K (bf16: its position-order copy with a
 // 3-D tile order, V from the regrouped copy; fp32: K and V read through the
 // order).
-sa_status run_taylor(const Req& r, const void* k, const void* v, void* ws, hipStream_t st) {
+sa_status run_taylor(const Req& r, const void* k, const void* v, const float* k_scale, void* ws,
+                     hipStream_t st) {
   sa::TaylorArgs a{};
   a.qbar = at<float>(ws, r.ws.qbar);
   a.kbar = at<float>(ws, r.ws.kbar);
@@ -249,7 +248,12 @@ sa_status run_taylor(const Req& r, const void* k, const void* v, void* ws, hipSt
     a.tm = r.tm;
     a.vprime32 = at<float>(ws, r.ws.vprime);
   } else {
-    a.k = static_cast<const uint16_t*>(r.tm.on ? at<uint16_t>(ws, r.ws.kpos16) : k);
+    if (r.qk == SA_FP8_E4M3) {
+      a.k8 = static_cast<const uint8_t*>(k);   // fp8 Q/K have no 3-D tile order
+      a.k_scale = k_scale;
+    } else {
+      a.k = static_cast<const uint16_t*>(r.tm.on ? at<uint16_t>(ws, r.ws.kpos16) : k);
+    }
     a.vt16 = at<uint16_t>(ws, r.ws.vt16);
     a.vprime = at<uint16_t>(ws, r.ws.vprime);
   }
@@ -267,7 +271,7 @@ sa_status run_pool(const Req& r, const sa_inputs* in, void* ws, hipStream_t st) 
   sa_status s;
   if ((s = hip_status(sa::launch_pool(pool_args(r, in, ws, false), st), "pool kernel launch")) != SA_OK)
     return s;
-  return r.correction == 2 ? run_taylor(r, in->k, in->v, ws, st) : s;
+  return r.correction == 2 ? run_taylor(r, in->k, in->v, in->k_scale, ws, st) : s;
 }
 
 sa_status run_attn(const Req& r, const sa_inputs* in, void* o, float* lse, int32_t* kept, void* ws,
@@ -413,7 +417,7 @@ SA_API sa_status sa_qk_prologue(const sa_shape* shape, const sa_params* params, 
   a.pro.Hg = r.Hg;
   a.pro.Wg = r.Wg;
   if ((s = hip_status(sa::launch_pool(a, (hipStream_t)stream), "producer kernel launch")) != SA_OK) return s;
-  return r.correction == 2 ? run_taylor(r, k_out, in->v, ws, (hipStream_t)stream) : s;
+  return r.correction == 2 ? run_taylor(r, k_out, in->v, nullptr, ws, (hipStream_t)stream) : s;
 }
 
 SA_API sa_status sa_dense_forward(const sa_shape* shape, float scale, const sa_inputs* in, void* o,

@@ -203,7 +203,7 @@ __global__ __launch_bounds__(128 * QB, QB == 2 ? 2 : 1) void attn_kernel(AttnArg
   constexpr int SMEM_PROXY = SPARSE ? QB * kMaxNb * 4 : 0;
   constexpr int SMEM = SMEM_STAGE > SMEM_PROXY ? SMEM_STAGE : SMEM_PROXY;
   static_assert(KI8 >= 1 && VI >= 1, "tile copies per wave");
-  static_assert(!TAY || (SPARSE && !FP8), "first-order values: sparse bf16 only");
+  static_assert(!TAY || SPARSE, "first-order values: sparse only");
 
   __shared__ __attribute__((aligned(1024))) uint8_t smem[SMEM];
   __shared__ uint8_t flags[SPARSE ? kMaxNb : 1];
@@ -662,11 +662,9 @@ hipError_t launch_d(const AttnArgs& a, hipStream_t st) {
   constexpr int STG = SA_STAGES;
   const int ngroups = (a.Nb + QB - 1) / QB;
   const dim3 grid((unsigned)(a.BH * ngroups));
-  if constexpr (!FP8) {
-    if (a.sparse && a.vprime) {
-      hipLaunchKernelGGL((attn_kernel<D, true, false, QB, STG, true>), grid, dim3(128 * QB), 0, st, a);
-      return hipGetLastError();
-    }
+  if (a.sparse && a.vprime) {
+    hipLaunchKernelGGL((attn_kernel<D, true, FP8, QB, STG, true>), grid, dim3(128 * QB), 0, st, a);
+    return hipGetLastError();
   }
   if (a.sparse)
     hipLaunchKernelGGL((attn_kernel<D, true, FP8, QB, STG>), grid, dim3(128 * QB), 0, st, a);

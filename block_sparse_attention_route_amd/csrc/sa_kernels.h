@@ -59,6 +59,8 @@ struct TaylorArgs {
   const float* vf;
   TileMap tm;
   float* vprime32;       // float32: [BH][Nb][Nb][D]
+  const uint8_t* k8;     // fp8 e4m3 K codes [BH][N][D] (with k_scale), else null
+  const float* k_scale;  // [BH][Nb]
 };
 
 struct RouteArgs {

@@ -30,7 +30,10 @@
 //                           at vbar_J, V_J^T from the regrouped V
 // and writes V' in bf16.  The K and V^T tiles of the next key block are
 // fetched into registers while the current one is used and handed over
-// through a second LDS buffer, so one barrier per key block suffices.  Each
+// through a second LDS buffer, so one barrier per key block suffices.  With
+// fp8 K the codes are widened to bf16 (exactly) on their way into LDS and the
+// block scale multiplies the score accumulator (S~ = scale_J * (codes . qc) -
+// r_IJ, the block mean kbar_J being that of the dequantised keys).  Each
 // wave turns its 32 output rows around in LDS and writes them as whole rows,
 // 16 bytes per lane (written straight from the MFMA layout, every store
 // would touch 32 rows).
@@ -55,9 +58,11 @@ struct TyCfg {
   static constexpr int KLD = KTILE / 16 / kTyThreads;  // 16-byte copies per thread
   static constexpr int VLD = VTILE / 16 / kTyThreads;
   static constexpr int OST = 32 * KROW / 16 / 64;   // 16-byte output stores per lane: 32 rows of D bf16
+  static constexpr int K8C = 64 * D / 16;             // 16-byte chunks of an fp8 K tile
+  static constexpr int KLD8 = (K8C + kTyThreads - 1) / kTyThreads;
 };
 
-template <int D>
+template <int D, bool K8>
 __global__ __launch_bounds__(kTyThreads, 1) void taylor_kernel(TaylorArgs a) {
   using C = TyCfg<D>;
   static_assert(C::KLD >= 1 && C::VLD >= 1, "tile copies per thread");
@@ -106,15 +111,26 @@ __global__ __launch_bounds__(kTyThreads, 1) void taylor_kernel(TaylorArgs a) {
 
   // Copies of key block J: per thread KLD + VLD 16-byte chunks of the K and
   // V^T tiles, and one of the kbar / vbar rows for the first D/2 threads.
-  u32x4 kr[C::KLD], vr[C::VLD], mr;
+  u32x4 kr[K8 ? C::KLD8 : C::KLD], vr[C::VLD], mr;
   auto fetch = [&](int J) {
     const int nJ = (J == Nb - 1) ? ntail : kBlock;
-    const uint16_t* kbase = a.k + ((size_t)bh * N + (size_t)J * kBlock) * D;
+    if constexpr (K8) {
+      // fp8 codes, 16 per chunk, in row order (the swizzle is applied when stored)
+      const uint8_t* kbase = a.k8 + ((size_t)bh * N + (size_t)J * kBlock) * D;
 #pragma unroll
-    for (int i = 0; i < C::KLD; ++i) {
-      const int P = tid + kTyThreads * i, row = P / C::CPR, pc = P % C::CPR;
-      const int src_row = min(row, nJ - 1);   // rows past the sequence end: finite data, zeroed later
-      kr[i] = *reinterpret_cast<const u32x4*>(kbase + (size_t)src_row * D + swz<C::CPR>(row, pc) * 8);
+      for (int i = 0; i < C::KLD8; ++i) {
+        const int P = tid + kTyThreads * i, row = P / (D / 16), pc = P % (D / 16);
+        if (P < C::K8C)
+          kr[i] = *reinterpret_cast<const u32x4*>(kbase + (size_t)min(row, nJ - 1) * D + pc * 16);
+      }
+    } else {
+      const uint16_t* kbase = a.k + ((size_t)bh * N + (size_t)J * kBlock) * D;
+#pragma unroll
+      for (int i = 0; i < C::KLD; ++i) {
+        const int P = tid + kTyThreads * i, row = P / C::CPR, pc = P % C::CPR;
+        const int src_row = min(row, nJ - 1);   // rows past the sequence end: finite data, zeroed later
+        kr[i] = *reinterpret_cast<const u32x4*>(kbase + (size_t)src_row * D + swz<C::CPR>(row, pc) * 8);
+      }
     }
     const uint16_t* vbase = a.vt16 + ((size_t)bh * Nb + J) * D * kBlock;
 #pragma unroll
@@ -128,10 +144,28 @@ __global__ __launch_bounds__(kTyThreads, 1) void taylor_kernel(TaylorArgs a) {
     }
   };
   auto stash = [&](int buf) {
+    if constexpr (K8) {
 #pragma unroll
-    for (int i = 0; i < C::KLD; ++i) {
-      const int P = tid + kTyThreads * i;
-      *reinterpret_cast<u32x4*>(&kt[buf][16 * P]) = kr[i];
+      for (int i = 0; i < C::KLD8; ++i) {
+        const int P = tid + kTyThreads * i, row = P / (D / 16), pc = P % (D / 16);
+        if (P < C::K8C) {
+          // 16 codes -> two bf16 chunks (exact), logical chunks 2 pc and 2 pc + 1
+#pragma unroll
+          for (int half = 0; half < 2; ++half) {
+            bf16x8 x;
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+              x[e] = static_cast<__bf16>(fp8e4m3_to_f32((kr[i][2 * half + (e >> 2)] >> (8 * (e & 3))) & 0xFFu));
+            *reinterpret_cast<bf16x8*>(&kt[buf][row * C::KROW + swz<C::CPR>(row, 2 * pc + half) * 16]) = x;
+          }
+        }
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < C::KLD; ++i) {
+        const int P = tid + kTyThreads * i;
+        *reinterpret_cast<u32x4*>(&kt[buf][16 * P]) = kr[i];
+      }
     }
 #pragma unroll
     for (int i = 0; i < C::VLD; ++i) {
@@ -197,12 +231,14 @@ __global__ __launch_bounds__(kTyThreads, 1) void taylor_kernel(TaylorArgs a) {
       }
       const float r = rp + __shfl_xor(rp, 32);
 
-      // S~^T = K_J qc^T - r_IJ
+      // S~^T = K_J qc^T - r_IJ (fp8: scale_J * (codes qc^T) - r_IJ, below)
+      float sk = 1.f;
+      if constexpr (K8) sk = a.k_scale[(size_t)bh * Nb + J];
       f32x16 sc[2];
 #pragma unroll
       for (int k2 = 0; k2 < 2; ++k2)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) sc[k2][e] = -r;
+        for (int e = 0; e < 16; ++e) sc[k2][e] = K8 ? 0.f : -r;
 #pragma unroll
       for (int ks = 0; ks < C::KS; ++ks) {
 #pragma unroll
@@ -222,13 +258,15 @@ __global__ __launch_bounds__(kTyThreads, 1) void taylor_kernel(TaylorArgs a) {
 #pragma unroll
           for (int e = 0; e < 16; ++e) {
             const bool live = 32 * k2 + key_of(e, h) < ntail;
-            pb[2 * k2 + (e >> 3)][e & 7] = static_cast<__bf16>(live ? sc[k2][e] * f : 0.f);
+            const float x = K8 ? fmaf(sk, sc[k2][e], -r) : sc[k2][e];
+            pb[2 * k2 + (e >> 3)][e & 7] = static_cast<__bf16>(live ? x * f : 0.f);
           }
       } else {
 #pragma unroll
         for (int k2 = 0; k2 < 2; ++k2)
 #pragma unroll
-          for (int e = 0; e < 16; ++e) pb[2 * k2 + (e >> 3)][e & 7] = static_cast<__bf16>(sc[k2][e]);
+          for (int e = 0; e < 16; ++e)
+            pb[2 * k2 + (e >> 3)][e & 7] = static_cast<__bf16>(K8 ? fmaf(sk, sc[k2][e], -r) : sc[k2][e]);
       }
 
       // V'^T = vbar_J + V_J^T S~^T
@@ -321,7 +359,10 @@ template <int D>
 hipError_t launch_d(const TaylorArgs& a, hipStream_t st) {
   const int nit = (a.Nb + kTyRows - 1) / kTyRows;
   const dim3 grid((unsigned)(a.BH * (a.Nbp / 64) * nit));
-  hipLaunchKernelGGL(taylor_kernel<D>, grid, dim3(kTyThreads), 0, st, a);
+  if (a.k8)
+    hipLaunchKernelGGL((taylor_kernel<D, true>), grid, dim3(kTyThreads), 0, st, a);
+  else
+    hipLaunchKernelGGL((taylor_kernel<D, false>), grid, dim3(kTyThreads), 0, st, a);
   return hipGetLastError();
 }
 

@@ -97,11 +97,10 @@ typedef struct sa_shape {
  * Attention").  Read here as the expansion of exp(s q_i . k_j) to first order
  * in the key's deviation d_j = k_j - kbar_J, coefficient taken at the query
  * block mean: a skipped block keeps the weight n_J exp(s q_i . kbar_J) and
- * takes the value vbar_J + (s / n_J) sum_j (qbar_I . d_j) v_j.  Needs bf16 or
- * fp32 Q/K/V (fp8 Q/K: SA_ERR_UNSUPPORTED); the pool step then also writes
- * these values, one D-vector per (query block, key block), and the workspace
- * grows by B*H*Nb*Nbp*D bf16 (Nbp = Nb rounded up to 64), or B*H*Nb*Nb*D
- * fp32 for fp32 inputs.
+ * takes the value vbar_J + (s / n_J) sum_j (qbar_I . d_j) v_j (fp8 keys:
+ * dequantised).  The pool step then also writes these values, one D-vector
+ * per (query block, key block), and the workspace grows by B*H*Nb*Nbp*D bf16
+ * (Nbp = Nb rounded up to 64), or B*H*Nb*Nb*D fp32 for fp32 inputs.
  * scale: softmax scale s; <= 0 selects 1/sqrt(D); must be finite.
  * topk: 0 = threshold routing with tau; > 0 = fixed budget instead: every
  * query block keeps the min(topk, Nb) key blocks of largest proxy, equal

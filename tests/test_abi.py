@@ -174,9 +174,13 @@ def test_tile_order_with_fp8_is_unsupported(lib):
     assert api.status_name(st) == "SA_ERR_UNSUPPORTED"
 
 
-def test_first_order_correction_with_fp8_is_unsupported(lib):
-    inp = _inputs(qk=api.SA_FP8_E4M3, v=api.SA_BF16, qs=FAKE, ks=FAKE)
-    assert api.status_name(_fwd(lib, _shape(), _params(corr=2), inp)) == "SA_ERR_UNSUPPORTED"
+def test_first_order_workspace_with_fp8_keys(lib):
+    # fp8 Q/K with bf16 V: bf16 values per (query block, key block), as for bf16
+    sh = _shape(B=1, H=2, T=1, Hg=10, Wg=13, D=64)       # N = 130: Nb = 3, Nbp = 64
+    inp = _inputs(qk=api.SA_FP8_E4M3, v=api.SA_BF16)
+    n1 = lib.sa_workspace_bytes(ctypes.byref(sh), ctypes.byref(_params()), ctypes.byref(inp))
+    n2 = lib.sa_workspace_bytes(ctypes.byref(sh), ctypes.byref(_params(corr=2)), ctypes.byref(inp))
+    assert n1 > 0 and n2 - n1 == (2 * 3 * 64 * 64 * 2 + 255) // 256 * 256
 
 
 def test_first_order_workspace_holds_values_per_block_pair(lib):

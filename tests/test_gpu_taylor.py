@@ -3,9 +3,9 @@ oracle.
 
 * seeded cases spanning several tiles and a ragged tail: D = 128 and 64,
   threshold and fixed budget, raster and 3-D tile order, batch and heads
-  above one, explicit scale, bf16 and float32 inputs: masks and every row's O
-  and LSE against the oracle's first-order model (float32 at its 1e-5
-  bounds);
+  above one, explicit scale, bf16, float32 and fp8 Q/K inputs: masks and
+  every row's O and LSE against the oracle's first-order model (float32 at
+  its 1e-5 bounds, fp8 at its 4e-2 bound);
 * the first-order values themselves (the section sa_pool appends to the
   workspace) against oracle.first_order_value for every (query block, key
   block) pair of a case, padding rows zero;
@@ -42,6 +42,9 @@ CASES = [
     # float32 inputs: the float32 path, at its tighter tolerances
     ("f32_d64_tau1", 1, 2, (2, 12, 13), 64, 1.0, 0, None, 0.0, 39, "f32"),
     ("f32_d128_topk3_tiles", 2, 1, (4, 8, 12), 128, 0.0, 3, (2, 4, 8), 0.0, 40, "f32"),
+    # fp8 e4m3 Q/K with block scales, bf16 V
+    ("fp8_d128_tau1", 2, 1, (3, 10, 13), 128, 1.0, 0, None, 0.0, 41, "fp8"),
+    ("fp8_d64_topk2", 1, 2, (2, 14, 11), 64, 0.0, 2, None, 0.0, 42, "fp8"),
 ]
 
 
@@ -50,19 +53,19 @@ def _run(case, corr):
     dtype = case[10] if len(case) > 10 else "bf16"
     wl = synth.Workload(name, B, H, *grid, D, dtype, (tau,), True, seed=seed)
     inp = synth.generate(wl)
-    q, k, v, _, _ = to_gpu(inp)
-    kw = dict(tau=tau, topk=topk, tile=tile, scale=scale)
+    q, k, v, qs, ks = to_gpu(inp)
+    kw = dict(tau=tau, topk=topk, tile=tile, scale=scale, q_scale=qs, k_scale=ks)
     ws = api.sa_pool(q, k, v, grid, correction=corr, **kw)
     o, lse, kept = api.sa_forward_pooled(q, k, v, grid, workspace=ws, correction=corr, want_kept=True, **kw)
-    return wl, inp, (q, k, v), ws, o, lse, kept
+    return wl, inp, (q, k, v, qs, ks), ws, o, lse, kept
 
 
 @pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
 def test_first_order_parity(case):
     name, B, H, grid, D, tau, topk, tile, scale, seed = case[:10]
     say(f"case {case}")
-    wl, inp, (q, k, v), ws, o, lse, kept = _run(case, 2)
-    mask, kept_r = api.sa_route(q, k, v, grid, tau=tau, topk=topk, tile=tile, scale=scale)
+    wl, inp, (q, k, v, qs, ks), ws, o, lse, kept = _run(case, 2)
+    mask, kept_r = api.sa_route(q, k, v, grid, tau=tau, topk=topk, tile=tile, scale=scale, q_scale=qs, k_scale=ks)
     torch.cuda.synchronize()
     assert torch.equal(kept.cpu(), kept_r.cpu())
     m = mask.cpu().numpy()
@@ -78,14 +81,18 @@ def test_first_order_parity(case):
             say(f"  head ({b},{h}): {st}")
 
 
-@pytest.mark.parametrize("case", [CASES[0], CASES[3], CASES[5]], ids=[CASES[i][0] for i in (0, 3, 5)])
+VALUE_CASES = [CASES[0], CASES[3], CASES[5]] + [c for c in CASES if len(c) > 10 and c[10] == "fp8"]
+
+
+@pytest.mark.parametrize("case", VALUE_CASES, ids=[c[0] for c in VALUE_CASES])
 def test_first_order_values(case):
-    """The workspace's first-order values against the oracle, every pair."""
+    """The workspace's first-order values against the oracle, every pair
+    (fp8: of the dequantised keys)."""
     name, B, H, grid, D, tau, topk, tile, scale, seed = case[:10]
     say(f"case {case}")
-    wl, inp, (q, k, v), ws, _, _, _ = _run(case, 2)
+    wl, inp, (q, k, v, qs, ks), ws, _, _, _ = _run(case, 2)
     torch.cuda.synchronize()
-    off = api.sa_workspace_bytes(q, k, v, grid, tile=tile, correction=1)
+    off = api.sa_workspace_bytes(q, k, v, grid, qs, ks, tile=tile, correction=1)
     Nb = wl.Nb
     Nbp = (Nb + 63) // 64 * 64
     n = B * H * Nb * Nbp * D
@@ -121,13 +128,16 @@ def test_first_order_values(case):
             assert (err <= bound).all()
 
 
-@pytest.mark.parametrize("case", [c for c in CASES if len(c) > 10], ids=[c[0] for c in CASES if len(c) > 10])
+F32_CASES = [c for c in CASES if len(c) > 10 and c[10] == "f32"]
+
+
+@pytest.mark.parametrize("case", F32_CASES, ids=[c[0] for c in F32_CASES])
 def test_first_order_values_f32(case):
     """Float32 path: its values section ([BH][Nb][Nb][D] float) against the
     oracle, every pair, at float32 rounding."""
     name, B, H, grid, D, tau, topk, tile, scale, seed = case[:10]
     say(f"case {case}")
-    wl, inp, (q, k, v), ws, _, _, _ = _run(case, 2)
+    wl, inp, (q, k, v, qs, ks), ws, _, _, _ = _run(case, 2)
     torch.cuda.synchronize()
     off = api.sa_workspace_bytes(q, k, v, grid, tile=tile, correction=1)
     Nb = wl.Nb
