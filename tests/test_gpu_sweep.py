@@ -1,7 +1,7 @@
 """A seeded sweep of GPU parity over the option space (CPU oracle as the
 reference): random small grids (ragged and exact block counts), head
-dimension, dtype path, threshold or fixed budget, correction on or off, raster
-or 3-D tile order, explicit scale, batch and heads.  The draws are fixed by
+dimension, dtype path, threshold or fixed budget, correction off, mean copies
+or first order, raster or 3-D tile order, explicit scale, batch and heads.  The draws are fixed by
 the seed, so the same cases run every time; each one goes through sa_pool +
 sa_forward_pooled, and sa_route for the masks, as the benchmark does."""
 import math
@@ -32,6 +32,7 @@ def _draw(i):
     corr = bool(rng.random() < 0.7)
     scale = float(rng.choice([0.0, 0.0, 0.07]))
     B, H = int(rng.integers(1, 3)), int(rng.integers(1, 4))
+    corr = 2 if corr and rng.random() < 0.35 else int(corr)   # 2: the first-order correction
     return dict(dtype=dtype, D=D, grid=(T, Hg, Wg), tile=tile, topk=topk, tau=tau, corr=corr,
                 scale=scale, B=B, H=H, seed=2000 + i)
 
