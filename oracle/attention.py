@@ -58,10 +58,13 @@ It is evaluated here as the two-pass definition above in float64, not as an
 online softmax: first every logit of a row, then its max, then the sums.
 Each function below says which step it is.
 
-Pinned by tests/test_oracle_pins.py and tests/test_oracle_topk.py (closed
-forms of hand-derived cases, pure-Python brute force, library special cases,
-invariants); tests/test_oracle_mutants.py checks that planted mistakes fail
-those pins.  Parity unpinned: none.
+Pinned by tests/test_oracle_pins.py, tests/test_oracle_topk.py and
+tests/test_oracle_tiles.py (closed forms of hand-derived cases, pure-Python
+brute force, library special cases, invariants) and, for the first-order
+model, tests/test_oracle_taylor.py (per-key brute force, O(t^2) convergence
+to dense attention, reductions to the mean copies, invariants);
+tests/test_oracle_mutants.py and the mutants in test_oracle_taylor.py check
+that planted mistakes fail those pins.  Parity unpinned: none.
 """
 from __future__ import annotations
 
