@@ -18,7 +18,12 @@
 //      key kbar_J, value vbar_J and log-multiplicity log(n_J), and is masked
 //      for a query block that keeps J.  Its logit s * q_i . kbar_J is entry
 //      (i, J) of s * Q_I Kbar^T -- the below-threshold score column of block
-//      J -- and it enters the same running max / sum as the exact keys;
+//      J -- and it enters the same running max / sum as the exact keys.  With
+//      the first-order correction (TAY; the paper review of the Sol Video
+//      Inference Engine, xllm-io blog, five acceleration techniques, item
+//      "Sparse Attention": non-critical blocks compensated to first order)
+//      the value of virtual key J is its first-order value for this query
+//      block, V'[I][J] from the workspace, staged per query block in LDS;
 //   3. exact: flash attention over the kept key blocks (the union list; the
 //      waves of a query block that does not keep a block skip it), with the
 //      ragged last key block masked;
