@@ -159,6 +159,9 @@ def test_empty_calls_are_ok_without_pointers(lib, kw):
     assert st == 0
     st = lib.sa_dense_forward(ctypes.byref(sh), 0.0, ctypes.byref(inp), None, None, None, 0, None)
     assert st == 0
+    # the first-order correction: nothing to pool or correct either
+    assert _fwd(lib, sh, _params(corr=2), inp, o=None, lse=None, ws=None, ws_bytes=0) == 0
+    assert lib.sa_pool(ctypes.byref(sh), ctypes.byref(_params(corr=2)), ctypes.byref(inp), None, 0, None) == 0
 
 
 def test_params_struct_layout():
