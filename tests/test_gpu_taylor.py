@@ -13,6 +13,7 @@ oracle.
   changes the skipped blocks' values only, and the kernel takes the same
   weights, so the two agree bit for bit;
 * the fused producer step followed by the first-order path;
+* the maximum sequence length (N = 262,144, Nb = 4096);
 * the 720p size (B = 1, H = 40, 21 x 45 x 80, bf16) at tau = 2, the
   configuration the benchmark times for this mode: masks of every head, O
   and LSE of sampled query blocks of four heads.
@@ -194,6 +195,26 @@ def test_producer_then_first_order():
     ws2 = api.sa_pool(qo, ko, v, grid, tau=1.0, correction=2)
     torch.cuda.synchronize()
     assert torch.equal(ws, ws2)
+
+
+def test_first_order_maximum_sequence_length():
+    """N = 262,144 tokens (Nb = 4096, the on-chip routing limit; 64 correction
+    tiles per query block), sampled query blocks incl. the last ones."""
+    grid = (64, 64, 64)
+    wl = synth.Workload("max_first_order", 1, 1, *grid, 128, "bf16", (2.0,), True, seed=43)
+    assert wl.N == api.MAX_N
+    say("case first-order N = MAX_N")
+    inp = synth.generate(wl)
+    q, k, v, _, _ = to_gpu(inp)
+    ws = api.sa_pool(q, k, v, grid, tau=2.0, correction=2)
+    o, lse, kept = api.sa_forward_pooled(q, k, v, grid, tau=2.0, correction=2, workspace=ws, want_kept=True)
+    mask, kept_r = api.sa_route(q, k, v, grid, tau=2.0)
+    torch.cuda.synchronize()
+    assert torch.equal(kept.cpu(), kept_r.cpu())
+    del ws
+    keep, _, _ = mask_check(inp, 0, 0, mask[0, 0].cpu().numpy(), 2.0)
+    st = output_check(inp, 0, 0, o, lse, keep, 2.0, 2, qblocks=[0, 2047, 4094, 4095])
+    say(f"  {st}")
 
 
 _WL = None
