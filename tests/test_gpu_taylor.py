@@ -11,7 +11,8 @@ oracle.
   block) pair of a case, padding rows zero;
 * LSE against the mean copies' run on the same inputs: the first-order model
   changes the skipped blocks' values only, and the kernel takes the same
-  weights, so the two agree bit for bit;
+  weights, so the two agree bit for bit; with tau = inf (nothing skipped) O
+  agrees bit for bit too;
 * the fused producer step followed by the first-order path;
 * the maximum sequence length (N = 262,144, Nb = 4096);
 * the 720p size (B = 1, H = 40, 21 x 45 x 80, bf16) at tau = 2, the
@@ -174,6 +175,18 @@ def test_lse_equals_mean_copies(case):
     torch.cuda.synchronize()
     assert torch.equal(lse1, lse2)
     assert not torch.equal(o1, o2)
+
+
+def test_keep_all_equals_mean_copies():
+    """tau = inf skips nothing: the first-order run equals the mean copies' bit
+    for bit (its correction tiles are all masked)."""
+    case = ("keep_all", 1, 2, (3, 10, 13), 128, math.inf, 0, None, 0.0, 44)
+    say(f"case {case}")
+    _, _, _, _, o2, lse2, kept = _run(case, 2)
+    _, _, _, _, o1, lse1, _ = _run(case, 1)
+    torch.cuda.synchronize()
+    assert (kept.cpu() == kept.shape[-1]).all()
+    assert torch.equal(o1, o2) and torch.equal(lse1, lse2)
 
 
 def test_producer_then_first_order():
