@@ -17,7 +17,9 @@
  *            (or, with a fixed budget topk, the topk largest p_IJ of row I)
  *   exact    logits s * q_i . k_j for the tokens j of kept blocks
  *   correct  each skipped J acts as n_J copies of (kbar_J, vbar_J): logit
- *            s * q_i . kbar_J with weight n_J (only if correction != 0)
+ *            s * q_i . kbar_J with weight n_J (only if correction != 0);
+ *            with correction == 2 the value is instead the first-order one,
+ *            vbar_J + (s / n_J) sum_j (qbar_I . (k_j - kbar_J)) v_j
  *   output   o_i = softmax-weighted sum of values over all those logits,
  *            lse_i = natural-log log-sum-exp of the weighted logits.
  *
