@@ -17,7 +17,8 @@ oracle.
 * the maximum sequence length (N = 262,144, Nb = 4096);
 * the 720p size (B = 1, H = 40, 21 x 45 x 80, bf16) at tau = 2, the
   configuration the benchmark times for this mode: masks of every head, O
-  and LSE of sampled query blocks of four heads.
+  and LSE of sampled query blocks of four heads; and the 720p CFG fp8
+  configuration (B = 2) at tau = 4, two heads.
 """
 import math
 
@@ -239,6 +240,30 @@ def _inputs_720p():
         wl = synth.workload("720p")
         _WL = (wl, synth.generate(wl))
     return _WL
+
+
+def test_first_order_720p_cfg_fp8():
+    """The 720p CFG configuration (B = 2, H = 40, fp8 e4m3 Q/K with block
+    scales, bf16 V) at its tau = 4 with the first-order correction: kept
+    counts of every head against sa_route, masks and sampled query blocks of
+    two heads (one per CFG batch) against the oracle."""
+    wl = synth.workload("720p_cfg_fp8")
+    tau = wl.taus[0]
+    say(f"case 720p CFG fp8 first-order tau={tau}")
+    inp = synth.generate(wl)
+    q, k, v, qs, ks = to_gpu(inp)
+    grid = (wl.T, wl.Hg, wl.Wg)
+    kw = dict(tau=tau, q_scale=qs, k_scale=ks)
+    ws = api.sa_pool(q, k, v, grid, correction=2, **kw)
+    o, lse, kept = api.sa_forward_pooled(q, k, v, grid, correction=2, workspace=ws, want_kept=True, **kw)
+    mask, kept_r = api.sa_route(q, k, v, grid, **kw)
+    torch.cuda.synchronize()
+    assert torch.equal(kept.cpu(), kept_r.cpu())
+    del ws, q, k, v
+    for (b, h) in [(0, 0), (1, wl.H - 1)]:
+        keep, _, _ = mask_check(inp, b, h, mask[b, h].cpu().numpy(), tau)
+        st = output_check(inp, b, h, o, lse, keep, tau, 2, qblocks=[0, 600, wl.Nb - 1])
+        say(f"  head ({b},{h}): {st}")
 
 
 def test_first_order_720p():
