@@ -23,8 +23,6 @@ LIBDIR = os.path.join(PKG, "_lib")
 LIB = os.path.join(LIBDIR, "libsa_route.so")
 
 SOURCES = ["api.cpp", "pool.hip", "route.hip", "taylor.hip", "attn_mfma.hip", "attn_f32.hip"]
-# standalone measurement programs (not part of the library)
-MICROBENCH = {"mfma_ceiling": os.path.join(PKG, "microbench", "mfma_ceiling.hip")}
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
@@ -36,10 +34,7 @@ COMMON = [
     f"-I{INCLUDE}", f"-I{CSRC}",
 ]
 
-
-# The LDS-DMA copies set M0 in inline assembly; the kernels make no other use
-# of M0, so the compiler's note about clobbering a reserved register is noise.
-EXTRA = {"attn_mfma.hip": ["-Wno-inline-asm"]}
+EXTRA: dict = {}
 
 
 def _compile(src: str) -> str:
@@ -68,13 +63,6 @@ def build(jobs: int | None = None, verbose: bool = True) -> str:
     if res.returncode != 0:
         raise RuntimeError(f"link failed: {' '.join(cmd)}\n{res.stdout}\n{res.stderr}")
     shutil.move(tmp, LIB)
-    for name, src in MICROBENCH.items():
-        exe = os.path.join(LIBDIR, name)
-        cmd = [HIPCC, "-O3", f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang",
-               "-packed-fp32-ops", src, "-o", exe]
-        res = subprocess.run(cmd, capture_output=True, text=True)
-        if res.returncode != 0:
-            raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{res.stdout}\n{res.stderr}")
     if verbose:
         print(f"built {LIB}")
     return LIB

@@ -136,11 +136,14 @@ struct Cfg {
 // bytes land at lds_wave_base + 16*l.  Issued as inline assembly so that the
 // compiler does not order every later LDS read behind the copy; the kernel
 // waits for each tile itself (vmcnt) before the barrier that publishes it.
+// The copy takes its LDS address from M0, which the compiler owns: the
+// statement saves M0 and restores it, so M0 is unchanged across it.
 __device__ __forceinline__ void dma16(const void* gsrc, uint32_t lds_wave_base) {
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
-               :
+  uint32_t saved;
+  asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %1, off\n\ts_mov_b32 m0, %0"
+               : "=&s"(saved)
                : "v"(gsrc), "s"(__builtin_amdgcn_readfirstlane(lds_wave_base))
-               : "memory", "m0");
+               : "memory");
 }
 
 // The same copy from a wave-uniform base address (scalar registers) plus a
@@ -153,10 +156,11 @@ __device__ __forceinline__ uint64_t uniform_addr(const void* p) {
   return ((uint64_t)hi << 32) | lo;
 }
 __device__ __forceinline__ void dma16s(uint32_t voff, uint64_t sbase, uint32_t lds_wave_base) {
-  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
-               :
+  uint32_t saved;
+  asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %3\n\tglobal_load_lds_dwordx4 %1, %2\n\ts_mov_b32 m0, %0"
+               : "=&s"(saved)
                : "v"(voff), "s"(sbase), "s"(__builtin_amdgcn_readfirstlane(lds_wave_base))
-               : "memory", "m0");
+               : "memory");
 }
 
 // One float from a wave-uniform global address through the scalar unit,
@@ -453,100 +457,78 @@ __global__ __launch_bounds__(128 * QB, QB == 2 ? 2 : 1) void attn_kernel(AttnArg
       return;
     }
 
-    // ---- S^T = K Q^T for the 64 keys of the tile (two 32-key MFMA tiles)
+    // ---- the tile in two halves of 32 keys (kt = 0, 1): each half's scores
+    // S^T = K Q^T, its weights and its part of O^T += V^T P^T.  The weights of
+    // one half are computed between the matrix products of the other, so
+    // that the vector ALU and the matrix core work side by side:
+    //   region 1: S^T of half 0, then S^T of half 1 || weights of half 0
+    //   region 2: PV of half 0                      || weights of half 1
+    //   region 3: PV of half 1
+    // Operands are read from LDS NPRE products ahead, and the source order is
+    // pinned with scheduling barriers.
     const uint8_t* Kb = smem + stg * C::STAGE;
     const uint8_t* Vb = Kb + C::KTILE;
+    float c2 = c2_base * qscale;
+    constexpr bool k8 = FP8 && !virt;
+    if constexpr (k8) c2 *= scalar_load_f32(a.k_scale + ((size_t)bh * Nb + J));
+    constexpr int KS = C::KS, DT = C::DT;
+    constexpr int NPRE = 4;
+    constexpr int PA = 8 / KS;        // weight pairs per product in region 1
+    constexpr int PB = 8 / (2 * DT);  // and in region 2
+    using KOp = typename std::conditional<k8, uint64_t, bf16x8>::type;
+    auto kop = [&](int i) __attribute__((always_inline)) {  // operand of product i of region 1
+      const int kt = i / KS, ks = i % KS;
+      const int krow = 32 * kt + kperm(l32);
+      if constexpr (k8)
+        return *reinterpret_cast<const uint64_t*>(Kb + krow * C::KROW8 + swz_any<C::CPR8>(krow, ks) * 16 + 8 * h);
+      else
+        return *reinterpret_cast<const bf16x8*>(Kb + krow * C::KROW16 + swz<C::CPR16>(krow, 2 * ks + h) * 16);
+    };
+    auto vop = [&](int i) __attribute__((always_inline)) {  // V^T operand of product i of regions 2-3
+      const int k4 = i / DT, dt = i % DT;
+      const int vrow = 32 * dt + l32;
+      return *reinterpret_cast<const bf16x8*>(Vb + vrow * 128 + swz<8>(vrow, 2 * k4 + h) * 16);
+    };
+
     f32x16 s[2];
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
       for (int r = 0; r < 16; ++r) s[kt][r] = 0.f;
-    float c2 = c2_base * qscale;
-    bool k8 = false;
-    if constexpr (FP8) {
-      if (!virt) {
-        k8 = true;
-        c2 *= scalar_load_f32(a.k_scale + ((size_t)bh * Nb + J));
-      }
-    }
-    if (k8) {
-      if constexpr (FP8) {
-#pragma unroll
-        for (int ks = 0; ks < C::KS; ++ks) {
-#pragma unroll
-          for (int kt = 0; kt < 2; ++kt) {
-            const int krow = 32 * kt + kperm(l32);
-            const uint64_t ka = *reinterpret_cast<const uint64_t*>(
-                Kb + krow * C::KROW8 + swz_any<C::CPR8>(krow, ks) * 16 + 8 * h);
-            s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_fp8_fp8((long)ka, (long)q8[ks], s[kt], 0, 0, 0);
-          }
-        }
-      }
-    } else {
-      bf16x8 ka[2][2];
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt) {
-        const int krow = 32 * kt + kperm(l32);
-        ka[0][kt] = *reinterpret_cast<const bf16x8*>(Kb + krow * C::KROW16 + swz<C::CPR16>(krow, h) * 16);
-      }
-#pragma unroll
-      for (int ks = 0; ks < C::KS; ++ks) {
-        if (ks + 1 < C::KS) {
-#pragma unroll
-          for (int kt = 0; kt < 2; ++kt) {
-            const int krow = 32 * kt + kperm(l32);
-            ka[(ks + 1) & 1][kt] = *reinterpret_cast<const bf16x8*>(
-                Kb + krow * C::KROW16 + swz<C::CPR16>(krow, 2 * (ks + 1) + h) * 16);
-          }
-        }
-#pragma unroll
-        for (int kt = 0; kt < 2; ++kt)
-          s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[ks & 1][kt], qr[ks], s[kt], 0, 0, 0);
-      }
-    }
-
-    // ---- masks and log-multiplicities, applied to the raw scores (c2 > 0)
-    if constexpr (KIND == kVirt) {
-      // 64 virtual keys J = 64*it + 32kt + key_of(r, h): live iff this query
-      // block skips J; weight log2(n_J) = 6, or log2 of the tail's size
-      const uint64_t bits = skipbits[qsel * (kMaxNb / 64) + it];
-      const float inv_c2 = 1.f / c2;
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int kk = 32 * kt + key_of(r, h);
-          const bool live = (bits >> kk) & 1u;
-          const float w = (64 * it + kk == Nb - 1) ? log2_tail : 6.0f;
-          s[kt][r] = live ? fmaf(w, inv_c2, s[kt][r]) : kNegInf;
-        }
-    } else if constexpr (KIND == kTail) {
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-        for (int r = 0; r < 16; ++r)
-          if (32 * kt + key_of(r, h) >= ntail) s[kt][r] = kNegInf;
-    }
-
-    // ---- online softmax (row = this lane's query; keys split with lane^32).
     bf16x8 pb[4];
-    float rs = 0.f;
+    float rs[2] = {0.f, 0.f};
     typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
     const bf16x2 ones = {static_cast<__bf16>(1.f), static_cast<__bf16>(1.f)};
-    // bf16 weights 2^(s*c2 - m) of this lane's 32 keys and their sum
-    auto weights = [&](float negm) __attribute__((always_inline)) {
-      rs = 0.f;
+    const float inv_c2 = 1.f / c2;
+    // Elements r, r+1 of half kt: the tile kind's masks and log-multiplicities
+    // (applied to the raw scores, c2 > 0, and written back), then the bf16
+    // weights 2^(s*c2 - m) and their sum.  Element r of half kt holds key
+    // 32kt + 8h + j(r), j(r) = r for r < 8 and r + 8 above.  The masks are
+    // applied once (MASK), not again when the weights are redone.
+    auto w_pair = [&](int kt, int r, float negm, auto maskc) __attribute__((always_inline)) {
+      constexpr bool MASK = decltype(maskc)::value;
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-        for (int r = 0; r < 16; r += 2) {
-          const __bf16 b0 = static_cast<__bf16>(__builtin_amdgcn_exp2f(fmaf(s[kt][r], c2, negm)));
-          const __bf16 b1 = static_cast<__bf16>(__builtin_amdgcn_exp2f(fmaf(s[kt][r + 1], c2, negm)));
-          pb[2 * kt + (r >> 3)][r & 7] = b0;
-          pb[2 * kt + (r >> 3)][(r & 7) + 1] = b1;
-          const bf16x2 pair = {b0, b1};
-          rs = __builtin_amdgcn_fdot2_f32_bf16(pair, ones, rs, false);
+      for (int e = 0; e < 2 && MASK; ++e) {
+        const int j = (r + e) < 8 ? (r + e) : (r + e) + 8;
+        if constexpr (KIND == kVirt) {
+          // virtual key J = 64*it + 32kt + 8h + j: live iff this query block
+          // skips J; weight log2(n_J) = 6, or log2 of the tail's size
+          const uint64_t bits = skipbits[qsel * (kMaxNb / 64) + it];
+          const uint32_t lb = (uint32_t)(bits >> (32 * kt + 8 * h));
+          const int jt = (Nb - 1) - 64 * it - 32 * kt - 8 * h;
+          const bool live = (lb >> j) & 1u;
+          const float w = (j == jt) ? log2_tail : 6.0f;
+          s[kt][r + e] = live ? fmaf(w, inv_c2, s[kt][r + e]) : kNegInf;
+        } else if constexpr (KIND == kTail) {
+          if (j >= ntail - 32 * kt - 8 * h) s[kt][r + e] = kNegInf;
         }
+      }
+      const __bf16 b0 = static_cast<__bf16>(__builtin_amdgcn_exp2f(fmaf(s[kt][r], c2, negm)));
+      const __bf16 b1 = static_cast<__bf16>(__builtin_amdgcn_exp2f(fmaf(s[kt][r + 1], c2, negm)));
+      pb[2 * kt + (r >> 3)][r & 7] = b0;
+      pb[2 * kt + (r >> 3)][(r & 7) + 1] = b1;
+      const bf16x2 pair = {b0, b1};
+      rs[kt] = __builtin_amdgcn_fdot2_f32_bf16(pair, ones, rs[kt], false);
     };
     auto raise_max = [&](float mt) __attribute__((always_inline)) {
       const float mn = fmaxf(m_run, mt);
@@ -554,57 +536,103 @@ __global__ __launch_bounds__(128 * QB, QB == 2 ? 2 : 1) void attn_kernel(AttnArg
       m_run = mn;
       l_run *= alpha;
 #pragma unroll
-      for (int dt = 0; dt < C::DT; ++dt)
+      for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[dt][r] *= alpha;
     };
-    auto tile_max = [&]() __attribute__((always_inline)) {
-      float mt = s[0][0];
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mt = fmaxf(mt, s[kt][r]);
-      return xor32_max(mt) * c2;
-    };
     // No per-tile maximum: the weights are taken against the maximum in use
-    // as it stands, and only a tile in which some row's weights exceed 2^64
+    // as it stands, and only a half in which some row's weights exceed 2^64
     // or are not finite -- its maximum lies more than 64 above the one in use
     // (log2 units), as on a row's first tile, where the maximum in use is
     // kMInit -- raises it and is redone.  Exact: numerator and denominator
     // share the maximum, and weights up to 2^64 keep their relative precision
     // in bf16 and in the fp32 sums (masked keys give 2^-inf = 0).
-    weights(-m_run);
-    if (__builtin_expect(__any(!(rs <= kWeightMax)), 0)) {
-      raise_max(tile_max());
-      weights(-m_run);
-    }
-    l_run += rs;
+    auto settle = [&](int kt) __attribute__((always_inline)) {
+      if (__builtin_expect(__any(!(rs[kt] <= kWeightMax)), 0)) {
+        float mt = s[kt][0];
+#pragma unroll
+        for (int r = 1; r < 16; ++r) mt = fmaxf(mt, s[kt][r]);
+        raise_max(xor32_max(mt) * c2);
+        rs[kt] = 0.f;
+#pragma unroll
+        for (int r = 0; r < 16; r += 2) w_pair(kt, r, -m_run, std::false_type{});
+      }
+      l_run += rs[kt];
+    };
+    auto mfma_s = [&](const KOp& ka, int ks, f32x16& c) __attribute__((always_inline)) {
+      if constexpr (k8)
+        c = __builtin_amdgcn_mfma_f32_32x32x16_fp8_fp8((long)ka, (long)q8[ks], c, 0, 0, 0);
+      else
+        c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qr[ks], c, 0, 0, 0);
+    };
 
-    // ---- O^T += V^T P^T
+    // region 1
+    KOp kb[NPRE];
+    bf16x8 vb[NPRE];
+#pragma unroll
+    for (int i = 0; i < NPRE; ++i) kb[i] = kop(i);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < 2 * KS; ++i) {
+      const int kt = i / KS;
+      mfma_s(kb[i % NPRE], i % KS, s[kt]);
+      if (i + NPRE < 2 * KS)
+        kb[i % NPRE] = kop(i + NPRE);
+      else if constexpr (!tv)
+        vb[i + NPRE - 2 * KS] = vop(i + NPRE - 2 * KS);
+      if (i >= KS) {
+        const float negm = -m_run;
+#pragma unroll
+        for (int p = 0; p < PA; ++p) w_pair(0, 2 * ((i - KS) * PA + p), negm, std::true_type{});
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    settle(0);
+
     if constexpr (tv) {
       // first-order values: key rows in LDS, gathered 8 keys per operand
+      // (lane: value column d = 32 dt + l32 of keys 16 k4 + 8 h + e)
       values_ready();
-      // lane: value column d = 32 dt + l32 of keys 16 k4 + 8 h + e
       const __bf16* vq = reinterpret_cast<const __bf16*>(vps + qsel * C::KTILE) + 8 * h * D + l32;
+      auto pv_gather = [&](int k4) __attribute__((always_inline)) {
 #pragma unroll
-      for (int dt = 0; dt < C::DT; ++dt) {
-#pragma unroll
-        for (int k4 = 0; k4 < 4; ++k4) {
+        for (int dt = 0; dt < DT; ++dt) {
           bf16x8 va;
 #pragma unroll
           for (int e = 0; e < 8; ++e) va[e] = vq[(16 * k4 + e) * D + 32 * dt];
           acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[k4], acc[dt], 0, 0, 0);
         }
+      };
+      pv_gather(0);
+      pv_gather(1);
+      {
+        const float negm = -m_run;
+#pragma unroll
+        for (int r = 0; r < 16; r += 2) w_pair(1, r, negm, std::true_type{});
       }
+      settle(1);
+      pv_gather(2);
+      pv_gather(3);
     } else {
+      // region 2
+      {
+        const float negm = -m_run;
 #pragma unroll
-      for (int dt = 0; dt < C::DT; ++dt) {
-        const int vrow = 32 * dt + l32;
+        for (int i = 0; i < 2 * DT; ++i) {
+          acc[i % DT] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vb[i % NPRE], pb[i / DT], acc[i % DT], 0, 0, 0);
+          vb[i % NPRE] = vop(i + NPRE);
 #pragma unroll
-        for (int k4 = 0; k4 < 4; ++k4) {
-          const bf16x8 va = *reinterpret_cast<const bf16x8*>(Vb + vrow * 128 + swz<8>(vrow, 2 * k4 + h) * 16);
-          acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[k4], acc[dt], 0, 0, 0);
+          for (int p = 0; p < PB; ++p) w_pair(1, 2 * (i * PB + p), negm, std::true_type{});
+          __builtin_amdgcn_sched_barrier(0);
         }
+      }
+      settle(1);
+      // region 3
+#pragma unroll
+      for (int i = 2 * DT; i < 4 * DT; ++i) {
+        acc[i % DT] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vb[i % NPRE], pb[i / DT], acc[i % DT], 0, 0, 0);
+        if (i + NPRE < 4 * DT) vb[i % NPRE] = vop(i + NPRE);
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
     };
