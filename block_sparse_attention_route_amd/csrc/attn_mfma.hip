@@ -283,14 +283,26 @@ __global__ __launch_bounds__(128 * QB, QB == 2 ? 2 : 1) void attn_kernel(AttnArg
   // position qrow holds token token_of(qrow): the raster order, or the 3-D tile order
   const size_t qtok = (size_t)bh * N + (rowvalid ? token_of(a.tm, qrow) : qrow);
   bf16x8 qr[C::KS];
-  uint64_t q8[FP8 ? C::KS : 1];
+  // fp8 Q codes as the B operand of v_mfma_f32_32x32x64_f8f6f4: product m
+  // contracts dims [64m, 64m + 64); lane half h holds the 32 codes of dims
+  // [64m + 32h, 64m + 32h + 32), the same dims its K operand holds
+  i32x8 q8[FP8 ? D / 64 : 1];
+  if constexpr (FP8) {
+    const uint8_t* qrow8 = reinterpret_cast<const uint8_t*>(a.q) + qtok * D;
+#pragma unroll
+    for (int m = 0; m < D / 64; ++m) {
+      i32x8 w = {};
+      if (rowvalid) w = *reinterpret_cast<const i32x8*>(qrow8 + 64 * m + 32 * h);
+      q8[m] = w;
+    }
+  }
 #pragma unroll
   for (int ks = 0; ks < C::KS; ++ks) {
     const int d0 = 16 * ks + 8 * h;
     if constexpr (FP8) {
+      // the codes widened exactly to bf16: the correction tiles' B operand
       uint64_t w = 0;
       if (rowvalid) w = *reinterpret_cast<const uint64_t*>(reinterpret_cast<const uint8_t*>(a.q) + qtok * D + d0);
-      q8[ks] = w;
       bf16x8 x;
 #pragma unroll
       for (int e = 0; e < 8; ++e) x[e] = static_cast<__bf16>(fp8e4m3_to_f32((uint32_t)(w >> (8 * e)) & 0xFFu));
@@ -472,17 +484,32 @@ __global__ __launch_bounds__(128 * QB, QB == 2 ? 2 : 1) void attn_kernel(AttnArg
     constexpr bool k8 = FP8 && !virt;
     if constexpr (k8) c2 *= scalar_load_f32(a.k_scale + ((size_t)bh * Nb + J));
     constexpr int KS = C::KS, DT = C::DT;
-    constexpr int NPRE = 4;
-    constexpr int PA = 8 / KS;        // weight pairs per product in region 1
-    constexpr int PB = 8 / (2 * DT);  // and in region 2
-    using KOp = typename std::conditional<k8, uint64_t, bf16x8>::type;
+    // products of S^T per half: D/16 bf16 MFMAs (K = 16), or D/64 fp8 ones
+    // (v_mfma_f32_32x32x64_f8f6f4, K = 64, twice the bf16 rate)
+    constexpr int NS = k8 ? D / 64 : KS;
+    constexpr int NPRE = 4;               // V^T operands in flight
+    constexpr int NPK = k8 ? 2 : NPRE;    // K operands in flight
+    constexpr int PA = 8 / NS;            // weight pairs per product in region 1
+    constexpr int PB = 8 / (2 * DT);      // and in region 2
+    using KOp = typename std::conditional<k8, i32x8, bf16x8>::type;
     auto kop = [&](int i) __attribute__((always_inline)) {  // operand of product i of region 1
-      const int kt = i / KS, ks = i % KS;
+      const int kt = i / NS, m = i % NS;
       const int krow = 32 * kt + kperm(l32);
-      if constexpr (k8)
-        return *reinterpret_cast<const uint64_t*>(Kb + krow * C::KROW8 + swz_any<C::CPR8>(krow, ks) * 16 + 8 * h);
-      else
-        return *reinterpret_cast<const bf16x8*>(Kb + krow * C::KROW16 + swz<C::CPR16>(krow, 2 * ks + h) * 16);
+      if constexpr (k8) {
+        // 32 codes: dims [64m + 32h, +32) of key row krow, two 16-byte chunks
+        const uint8_t* row = Kb + krow * C::KROW8;
+        const u32x4 lo = *reinterpret_cast<const u32x4*>(row + swz_any<C::CPR8>(krow, 4 * m + 2 * h) * 16);
+        const u32x4 hi = *reinterpret_cast<const u32x4*>(row + swz_any<C::CPR8>(krow, 4 * m + 2 * h + 1) * 16);
+        i32x8 k;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          k[e] = (int)lo[e];
+          k[4 + e] = (int)hi[e];
+        }
+        return k;
+      } else {
+        return *reinterpret_cast<const bf16x8*>(Kb + krow * C::KROW16 + swz<C::CPR16>(krow, 2 * m + h) * 16);
+      }
     };
     auto vop = [&](int i) __attribute__((always_inline)) {  // V^T operand of product i of regions 2-3
       const int k4 = i / DT, dt = i % DT;
@@ -559,31 +586,35 @@ __global__ __launch_bounds__(128 * QB, QB == 2 ? 2 : 1) void attn_kernel(AttnArg
       }
       l_run += rs[kt];
     };
-    auto mfma_s = [&](const KOp& ka, int ks, f32x16& c) __attribute__((always_inline)) {
+    auto mfma_s = [&](const KOp& ka, int m, f32x16& c) __attribute__((always_inline)) {
       if constexpr (k8)
-        c = __builtin_amdgcn_mfma_f32_32x32x16_fp8_fp8((long)ka, (long)q8[ks], c, 0, 0, 0);
+        // format codes 0, 0: both operands fp8 e4m3; no block-exponent scales
+        c = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ka, q8[m], c, 0, 0, 0, 0, 0, 0);
       else
-        c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qr[ks], c, 0, 0, 0);
+        c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qr[m], c, 0, 0, 0);
     };
 
     // region 1
-    KOp kb[NPRE];
+    KOp kb[NPK];
     bf16x8 vb[NPRE];
 #pragma unroll
-    for (int i = 0; i < NPRE; ++i) kb[i] = kop(i);
+    for (int i = 0; i < NPK; ++i) kb[i] = kop(i);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int i = 0; i < 2 * KS; ++i) {
-      const int kt = i / KS;
-      mfma_s(kb[i % NPRE], i % KS, s[kt]);
-      if (i + NPRE < 2 * KS)
-        kb[i % NPRE] = kop(i + NPRE);
-      else if constexpr (!tv)
-        vb[i + NPRE - 2 * KS] = vop(i + NPRE - 2 * KS);
-      if (i >= KS) {
+    for (int i = 0; i < 2 * NS; ++i) {
+      const int kt = i / NS;
+      mfma_s(kb[i % NPK], i % NS, s[kt]);
+      if (i + NPK < 2 * NS) {
+        kb[i % NPK] = kop(i + NPK);
+      } else if constexpr (!tv) {
+        // the first V^T operands of region 2, spread over the last products
+#pragma unroll
+        for (int v = (i + NPK - 2 * NS) * NPRE / NPK; v < (i + NPK - 2 * NS + 1) * NPRE / NPK; ++v) vb[v] = vop(v);
+      }
+      if (i >= NS) {
         const float negm = -m_run;
 #pragma unroll
-        for (int p = 0; p < PA; ++p) w_pair(0, 2 * ((i - KS) * PA + p), negm, std::true_type{});
+        for (int p = 0; p < PA; ++p) w_pair(0, 2 * ((i - NS) * PA + p), negm, std::true_type{});
       }
       __builtin_amdgcn_sched_barrier(0);
     }
