@@ -2,7 +2,7 @@
 """Benchmark of the on-the-fly block-sparse attention path on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 720p] [--tau 2]
-                    [--budgets 0.9,0.8]
+                    [--budgets 0.9,0.8] [--configs 720p:4,...] [--no-cpu-baseline]
 
 A step is one sa_forward call (pool kernel + fused route/correct/attend
 kernel) over the whole workload, inputs resident in HBM.  Prints one JSON
@@ -12,8 +12,9 @@ value = computed-block TFLOP/s: sum over kept (query block, key block) pairs
 of 4*D*n_I*n_J, divided by the wall time of one call.  The roofline object
 covers the fused kernel, timed with HIP events recorded on the stream the
 library launches on, around each launch inside the timed region.  The
-cpu_baseline leg times the float64 CPU oracle on a bounded sample of the same
-workload (a few query blocks of one head) and reports it in the same unit.
+cpu_baseline leg times the float64 CPU oracle on whole heads of the same
+workload (routing and attention of every query block of head (0, 0)) and
+reports it in the same unit.
 The fixed_budget list times the same call with routing by a fixed number of
 key blocks per query block (sparsity 0.9 and 0.8 by default) instead of tau;
 the tile_order list times it with blocks formed over 3-D tiles of the token
@@ -21,7 +22,16 @@ grid (4x4x4 and 1x8x8 by default); fused_producer times sa_qk_prologue (norm
 + rotary + pool of the Q/K projections) in place of the pool; first_order
 times the call with the first-order correction of the skipped blocks
 (correction = 2: the pool step also writes the per-pair values, the fused
-kernel reads them) and its error against dense attention.
+kernel reads them) and its error against dense attention.  The configs list
+repeats the call (a few steps each) at the other workloads: 720p at tau 4
+and 8, 480p, 1080p and the 720p CFG batch with fp8 Q/K, each with its dense
+call, density, and -- from the CPU leg -- the near-threshold and flipped
+block counts of every head.
+
+Pool bandwidth is quoted on the pass's algorithmic bytes (Q, K and V read
+once plus the three float32 mean tensors written, and the fp8 block scales),
+with this library's own layout bytes (bf16 key/value means and V regrouped
+per block, written for the attention kernel) beside them.
 """
 from __future__ import annotations
 
@@ -99,50 +109,91 @@ def correction_flops(mask: np.ndarray, N: int, D: int) -> float:
     return float(4.0 * D * (skipped * n[None, :]).sum())
 
 
-def cpu_baseline(inp, wl, tau, o_gpu, budget_s: float):
-    """Time the float64 oracle on a bounded sample: query blocks of head (0, 0)."""
-    from oracle import attention as orc  # test infrastructure: cpu_baseline leg only
+def _cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:  # pragma: no cover
+        pass
+    return "unknown"
+
+
+def _blas_threads() -> int:
     try:
         from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+        return max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
     except Exception:  # pragma: no cover
-        cores = 1
-    q, k, v = inp.head64(0, 0)
-    t0 = time.perf_counter()
-    keep, p, m = orc.route(q, k, wl.block, tau)
-    t_route = time.perf_counter() - t0
+        return 1
+
+
+def cpu_baseline(inp, wl, tau, o_gpu, heads: int = 1):
+    """Time the float64 oracle on whole heads of the workload: the routing of
+    every query block and the attention of every query block of heads
+    (0, 0), (0, 1), ...  One process; numpy's BLAS uses its thread pool."""
+    from oracle import attention as orc  # test infrastructure: cpu_baseline leg only
     ranges = orc.block_ranges(wl.N, wl.block)
     n = np.array([e - s for s, e in ranges], dtype=np.float64)
-    rng = np.random.default_rng(0)
-    order = [len(ranges) - 1] + list(rng.permutation(len(ranges) - 1))
-    flops, done, t_attend, maxerr = 0.0, [], 0.0, 0.0
-    o_g = o_gpu[0, 0].float().cpu().numpy()
-    for I in order:
+    flops, t_route, t_attend, maxerr, nband = 0.0, 0.0, 0.0, 0.0, 0
+    done = []
+    for hh in range(heads):
+        b, h = divmod(hh, wl.H)
+        q, k, v = inp.head64(b, h)
+        t0 = time.perf_counter()
+        keep, p, m = orc.route(q, k, wl.block, tau)
+        t_route += time.perf_counter() - t0
+        o_g = o_gpu[b, h].float().cpu().numpy()
         t1 = time.perf_counter()
-        a, b = ranges[I]
-        o_ref, _ = orc.attend_rows(q[a:b], k, v, keep[I], wl.block, wl.correction)
+        for I, (a0, a1) in enumerate(ranges):
+            o_ref, _ = orc.attend_rows(q[a0:a1], k, v, keep[I], wl.block, wl.correction)
+            maxerr = max(maxerr, float(np.abs(o_ref - o_g[a0:a1]).max()))
+            flops += 4.0 * wl.D * n[I] * float((keep[I] * n).sum())
         t_attend += time.perf_counter() - t1
-        flops += 4.0 * wl.D * n[I] * float((keep[I] * n).sum())
-        maxerr = max(maxerr, float(np.abs(o_ref - o_g[a:b]).max()))
-        done.append(I)
-        if t_route + t_attend > budget_s:
-            break
+        nband += int((np.abs(p - (m - tau)[:, None]) < 1e-3).sum()) if math.isfinite(tau) else 0
+        done.append((b, h))
     elapsed = t_route + t_attend
-    nband = int((np.abs(p - (m - tau)[:, None]) < 1e-3).sum()) if math.isfinite(tau) else 0
     return {
         "value": flops / elapsed / 1e12,
         "unit": "TFLOP/s",
-        "cores": int(cores),
+        "cores": _blas_threads(),
+        "cores_kind": "BLAS threads of one numpy process",
+        "host_cpus": len(os.sched_getaffinity(0)),
+        "cpu_model": _cpu_model(),
         "kind": "oracle",
-        "sample": (f"float64 numpy oracle, head (0,0) of {wl.name}: routing of all {len(ranges)} query blocks "
-                   f"({t_route:.2f} s) + attention of {len(done)} query blocks incl. the ragged last one "
-                   f"({t_attend:.2f} s); computed-block FLOP of the sample / time"),
+        "sample": (f"float64 numpy oracle, {len(done)} whole head(s) {done} of {wl.name}: routing of all "
+                   f"{len(ranges)} query blocks ({t_route:.2f} s) and attention of all {len(ranges)} query "
+                   f"blocks ({t_attend:.2f} s); computed-block FLOP of the sample / time"),
+        "sample_s": elapsed,
         "sample_max_abs_err_vs_gpu": maxerr,
-        # the whole call at the sample's rate per query block (routing per head
-        # scaled by the heads): an extrapolation, not a measurement
-        "extrapolated_call_s": (t_route + t_attend / len(done) * len(ranges)) * wl.B * wl.H,
-        "near_threshold_blocks_head0": nband,
+        # the whole call at the sample's rate per head: an extrapolation, not a measurement
+        "extrapolated_call_s": elapsed / len(done) * wl.B * wl.H,
+        "near_threshold_blocks_sampled_heads": nband,
     }
+
+
+def route_band_counts(inp, wl, tau, gpu_mask: np.ndarray) -> dict:
+    """The float64 routing of every head against the GPU's keep mask: blocks
+    whose proxy lies within 1e-3 of the threshold, how many of those the GPU
+    decided the other way, and differences outside that band (must be 0).
+    Runs in the cpu_baseline leg (it is the oracle's routing)."""
+    from oracle import attention as orc  # test infrastructure: cpu_baseline leg only
+    from concurrent.futures import ThreadPoolExecutor
+
+    def one(bh):
+        b, h = divmod(bh, wl.H)
+        q, k, _ = inp.head64(b, h)
+        keep, p, m = orc.route(q, k, wl.block, tau)
+        band = np.abs(p - (m - tau)[:, None]) < 1e-3
+        diff = gpu_mask[bh].astype(bool) != keep
+        return int(band.sum()), int((diff & band).sum()), int((diff & ~band).sum())
+
+    t0 = time.perf_counter()
+    with ThreadPoolExecutor(max_workers=8) as ex:
+        res = list(ex.map(one, range(wl.B * wl.H)))
+    return {"heads": wl.B * wl.H, "near_threshold_blocks": sum(r[0] for r in res),
+            "flipped_in_band": sum(r[1] for r in res), "differ_outside_band": sum(r[2] for r in res),
+            "oracle_routing_s": time.perf_counter() - t0}
 
 
 def approx_vs(o_s, l_s, od, lsed):
@@ -150,6 +201,103 @@ def approx_vs(o_s, l_s, od, lsed):
     d = o_s.float() - od.float()
     return {"o_rel_l2": float(d.norm() / od.float().norm()), "o_max_abs": float(d.abs().max()),
             "lse_mean_abs": float((l_s - lsed).abs().mean())}
+
+
+def peak_for(dtype: str) -> float:
+    if dtype == "fp8":
+        return 1.0 / (0.5 / PEAK_FP8_TFLOPS + 0.5 / PEAK_BF16_TFLOPS)   # QK^T fp8, PV bf16
+    return PEAK_BF16_TFLOPS
+
+
+def pool_algorithmic_bytes(wl) -> int:
+    """The pool pass's algorithmic bytes: Q, K, V read once (+ the fp8 block
+    scales) and the three float32 block-mean tensors written."""
+    bh = wl.B * wl.H
+    e_qk = {"f32": 4, "bf16": 2, "fp8": 1}[wl.dtype]
+    e_v = 4 if wl.dtype == "f32" else 2
+    b = bh * wl.N * wl.D * (2 * e_qk + e_v) + 3 * bh * wl.Nb * wl.D * 4
+    return b + (2 * bh * wl.Nb * 4 if wl.dtype == "fp8" else 0)
+
+
+def pool_layout_bytes(wl) -> int:
+    """Bytes the pool kernel of this library moves: the algorithmic bytes plus,
+    for bf16 V, the bf16 copies of the key/value means (padded to a multiple of
+    64 blocks) and V regrouped per 64-key block for the attention kernel."""
+    bh, nbp = wl.B * wl.H, (wl.Nb + 63) // 64 * 64
+    b = pool_algorithmic_bytes(wl)
+    if wl.dtype != "f32":
+        b += 2 * bh * nbp * wl.D * 2 + bh * wl.Nb * wl.D * 64 * 2
+    return b
+
+
+def time_config(name, tau, steps, dense_steps, cpu, inp=None, dev=None):
+    """One workload at one tau: sa_pool + sa_forward_pooled timed over `steps`
+    calls after a warm-up call, the dense call, density and (cpu) the oracle's
+    near-threshold / flipped counts over every head."""
+    wl = synth.workload(name)
+    t0 = time.time()
+    if inp is None:
+        inp = synth.generate(wl)
+    log(f"config {name} tau {tau:g}: inputs in {time.time() - t0:.1f}s")
+    q, k, v = inp.q.to(dev), inp.k.to(dev), inp.v.to(dev)
+    qs = inp.q_scale.to(dev) if inp.q_scale is not None else None
+    ks = inp.k_scale.to(dev) if inp.k_scale is not None else None
+    grid = (wl.T, wl.Hg, wl.Wg)
+    correction = wl.correction
+    ws = torch.empty(api.sa_workspace_bytes(q, k, v, grid), dtype=torch.uint8, device=dev)
+    o = torch.empty(q.shape, dtype=v.dtype, device=dev)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
+    kept = torch.empty((wl.B, wl.H, wl.Nb), dtype=torch.int32, device=dev)
+    mask, kept_r = api.sa_route(q, k, v, grid, tau=tau, q_scale=qs, k_scale=ks)
+    torch.cuda.synchronize()
+    mask_np = mask.cpu().numpy().reshape(wl.B * wl.H, wl.Nb, wl.Nb)
+    del mask
+    f_exact = computed_block_flops(mask_np, wl.N, wl.D)
+    f_dense = 4.0 * wl.B * wl.H * wl.N * wl.N * wl.D
+
+    def step():
+        api.sa_pool(q, k, v, grid, tau=tau, correction=correction, workspace=ws, q_scale=qs, k_scale=ks)
+        api.sa_forward_pooled(q, k, v, grid, tau=tau, correction=correction, workspace=ws, q_scale=qs,
+                              k_scale=ks, out=o, lse=lse, kept=kept, want_kept=True)
+    step()
+    torch.cuda.synchronize()
+    assert torch.equal(kept.cpu(), kept_r.cpu()), f"fused routing disagrees with sa_route ({name})"
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    peak = peak_for(wl.dtype)
+    rec = {"workload": name, "B": wl.B, "H": wl.H, "N": wl.N, "D": wl.D, "dtype": wl.dtype, "tau": tau,
+           "correction": correction, "steps": steps, "ms": ms,
+           "computed_block_tflops": f_exact / (ms * 1e-3) / 1e12,
+           "frac_peak": f_exact / (ms * 1e-3) / 1e12 / peak, "peak_tflops": peak,
+           "dense_equivalent_tflops": f_dense / (ms * 1e-3) / 1e12,
+           "block_density": float(mask_np.mean()), "union_inflation": union_inflation(mask_np),
+           "computed_block_tflop": f_exact / 1e12}
+    if dense_steps > 0:
+        od, lsed = torch.empty_like(o), torch.empty_like(lse)
+        wsd = torch.empty(max(api.sa_dense_workspace_bytes(q, k, v, grid), 1), dtype=torch.uint8, device=dev)
+        api.sa_dense_forward(q, k, v, grid, workspace=wsd, q_scale=qs, k_scale=ks, out=od, lse=lsed)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(dense_steps):
+            api.sa_dense_forward(q, k, v, grid, workspace=wsd, q_scale=qs, k_scale=ks, out=od, lse=lsed)
+        e1.record()
+        torch.cuda.synchronize()
+        dms = e0.elapsed_time(e1) / dense_steps
+        rec["dense_ms"] = dms
+        rec["dense_tflops"] = f_dense / (dms * 1e-3) / 1e12
+        rec["speedup_vs_dense"] = dms / ms
+        del od, lsed, wsd
+    del q, k, v, ws, o, lse, kept
+    torch.cuda.empty_cache()
+    if cpu:
+        rec["routing_vs_oracle"] = route_band_counts(inp, wl, tau, mask_np)
+    log(f"config {name} tau {tau:g}: {ms:.2f} ms, density {rec['block_density']:.3f}")
+    return rec
 
 
 def main() -> None:
@@ -161,7 +309,7 @@ def main() -> None:
     ap.add_argument("--tau", type=float, default=None)
     ap.add_argument("--no-correction", action="store_true")
     ap.add_argument("--dense-steps", type=int, default=2)
-    ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work")
+    ap.add_argument("--cpu-heads", type=int, default=1, help="whole heads of oracle work in cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--budgets", default="0.9,0.8",
                     help="fixed-budget routing sparsities to time as well (comma list, '' for none)")
@@ -170,6 +318,9 @@ def main() -> None:
                     help="3-D tile orders (t x h x w, product 64) to time at the same tau ('' for none)")
     ap.add_argument("--no-first-order", dest="first_order", action="store_false",
                     help="skip timing the first-order correction (correction = 2)")
+    ap.add_argument("--configs", default="720p:4,720p:8,480p:4,1080p:4,720p_cfg_fp8:4",
+                    help="other workloads to time as name:tau (comma list, '' for none)")
+    ap.add_argument("--config-steps", type=int, default=3)
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run one 1 GiB device-to-device copy (reference for the PMC byte counters)")
     args = ap.parse_args()
@@ -238,19 +389,9 @@ def main() -> None:
     value = f_exact / (ms_step * 1e-3) / 1e12
     fused_avg = float(np.mean(fused_ms))
     achieved = f_exact / (fused_avg * 1e-3) / 1e12
-    peak = PEAK_BF16_TFLOPS
-    if wl.dtype == "fp8":
-        peak = 1.0 / (0.5 / PEAK_FP8_TFLOPS + 0.5 / PEAK_BF16_TFLOPS)   # QK^T fp8, PV bf16
-    # pool: algorithmic bytes = Q, K, V read once (+ fp8 block scales), the three
-    # fp32 mean tensors, and for bf16 V the bf16 key/value means (padded to a
-    # multiple of 64 blocks) and V regrouped per 64-key block (padded to 64 rows)
-    bh, nbp = wl.B * wl.H, (wl.Nb + 63) // 64 * 64
-    e_qk = {"f32": 4, "bf16": 2, "fp8": 1}[wl.dtype]
-    e_v = 4 if wl.dtype == "f32" else 2
-    pool_bytes = bh * wl.N * wl.D * (2 * e_qk + e_v) + (2 * bh * wl.Nb * 4 if wl.dtype == "fp8" else 0)
-    pool_bytes += 3 * bh * wl.Nb * wl.D * 4
-    if wl.dtype != "f32":
-        pool_bytes += 2 * bh * nbp * wl.D * 2 + bh * wl.Nb * wl.D * 64 * 2
+    peak = peak_for(wl.dtype)
+    pool_bytes = pool_algorithmic_bytes(wl)
+    pool_lbytes = pool_layout_bytes(wl)
     pool_avg = float(np.mean(pool_ms))
 
     traffic = None
@@ -395,7 +536,7 @@ def main() -> None:
         e1.record()
         torch.cuda.synchronize()
         pms = e0.elapsed_time(e1) / args.budget_steps
-        pbytes = pool_bytes + 2 * wl.B * wl.H * wl.N * wl.D * 2       # + Q and K written back
+        pbytes = pool_lbytes + 2 * wl.B * wl.H * wl.N * wl.D * 2      # + Q and K written back
         producer = {"ms": pms, "gbs": pbytes / (pms * 1e-3) / 1e9,
                     "frac_hbm": pbytes / (pms * 1e-3) / 1e9 / PEAK_HBM_GBS, "bytes": pbytes,
                     "unfused_extra_bytes": 2 * wl.B * wl.H * wl.N * wl.D * 2}
@@ -461,7 +602,17 @@ def main() -> None:
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(inp, wl, tau, o, args.cpu_budget)
+        cpu = cpu_baseline(inp, wl, tau, o, args.cpu_heads)
+        cpu["routing_vs_oracle"] = route_band_counts(inp, wl, tau, mask_np)
+    del q, k, v, ws, o, lse, kept, ob, lseb
+    torch.cuda.empty_cache()
+
+    configs = []
+    for spec in [x for x in args.configs.split(",") if x.strip()]:
+        cname, ctau = spec.split(":")
+        same = cname == wl.name
+        configs.append(time_config(cname, float(ctau), args.config_steps, 1, not args.no_cpu_baseline,
+                                   inp=inp if same else None, dev=dev))
 
     out = {
         "metric": METRIC,
@@ -492,6 +643,8 @@ def main() -> None:
         "dense_equivalent_tflops": f_dense / (ms_step * 1e-3) / 1e12,
         "pool": {"ms": pool_avg, "gbs": pool_bytes / (pool_avg * 1e-3) / 1e9,
                  "frac_hbm": pool_bytes / (pool_avg * 1e-3) / 1e9 / PEAK_HBM_GBS, "bytes": pool_bytes,
+                 "bytes_kind": "algorithmic: Q, K, V read once + float32 block means written",
+                 "layout_bytes": pool_lbytes, "layout_gbs": pool_lbytes / (pool_avg * 1e-3) / 1e9,
                  "copy_1gib_gbs": (2 * (1 << 30) / (copy_ms * 1e-3) / 1e9) if copy_ms else None},
         "fused_kernel_ms": fused_avg,
         "ms_per_call_median": float(np.median(np.add(pool_ms, fused_ms))),
@@ -506,6 +659,7 @@ def main() -> None:
         "tile_order": tiled,
         "fused_producer": producer,
         "first_order": first_order,
+        "configs": configs,
         "cpu_baseline": cpu,
         "kernel_src": kernel_source_hash(),
     }

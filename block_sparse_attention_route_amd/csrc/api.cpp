@@ -176,6 +176,7 @@ sa::PoolArgs pool_args(const Req& r, const sa_inputs* in, void* ws, bool vt_only
   if (r.v == SA_BF16) a.vt16 = at<uint16_t>(ws, r.ws.vt16);
   if (!vt_only) {
     a.tm = r.tm;
+    a.sched = at<int>(ws, r.ws.sched);
     if (r.tm.on && r.qk == SA_BF16) a.kpos16 = at<uint16_t>(ws, r.ws.kpos16);
   }
   return a;
@@ -201,6 +202,7 @@ sa::AttnArgs attn_args(const Req& r, const sa_inputs* in, void* o, float* lse, i
   if (r.v == SA_BF16) a.vt16 = at<uint16_t>(ws, r.ws.vt16);
   if (sparse) {
     a.tm = r.tm;
+    a.sched = at<int>(ws, r.ws.sched);
     if (r.tm.on && r.qk == SA_BF16) a.kpos16 = at<uint16_t>(ws, r.ws.kpos16);
     if (r.correction == 2) {
       if (r.qk == SA_F32)

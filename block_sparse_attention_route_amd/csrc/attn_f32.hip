@@ -42,12 +42,12 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(AttnArgs a) {
   if constexpr (SPARSE) {
     for (int d = lane; d < D; d += 64) qb[d] = a.qbar[((size_t)bh * Nb + I) * D + d];
     __syncthreads();
-    proxy_rows<D, 64, 1>(qb, a.kbar + (size_t)bh * Nb * D, Nb, a.scale, 1, p);
+    proxy_rows<D, 64, 1>(qb, a.kbar + (size_t)bh * Nb * D, Nb, a.scale, 1, p, (int)threadIdx.x);
     __syncthreads();
     if (a.topk > 0)
-      topk_rows<64, 1>(p, Nb, 1, a.topk, flags, hist, sel, redi, counts);
+      topk_rows<64, 1>(p, Nb, 1, a.topk, flags, hist, sel, redi, counts, (int)threadIdx.x);
     else
-      threshold_rows<64, 1>(p, Nb, 1, a.tau, flags, redf, redi, counts);
+      threshold_rows<64, 1>(p, Nb, 1, a.tau, flags, redf, redi, counts, (int)threadIdx.x);
     if (a.kept && lane == 0) a.kept[(size_t)bh * Nb + I] = counts[0];
   }
 

@@ -58,6 +58,7 @@
 // bf16 and fp32 -- and makes the rescale rare (in practice a row's first
 // tile).  Row sums are taken over the bf16-rounded P that enters the PV
 // product.
+#include <algorithm>
 #include <type_traits>
 
 #include "sa_device.h"
@@ -92,9 +93,9 @@ __device__ __forceinline__ int swz_any(int row, int chunk) {
 
 template <int NT>
 __device__ __forceinline__ void build_union(const uint8_t* __restrict__ flags, int Nb,
-                                            uint16_t* __restrict__ ulist, int* total, int* wsum) {
+                                            uint16_t* __restrict__ ulist, int* total, int* wsum, int tid) {
   constexpr int NW = NT / 64;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63, wave = tid >> 6;
   const int seg = (Nb + NT - 1) / NT;
   const int j0 = min(Nb, tid * seg), j1 = min(Nb, j0 + seg);
   int cnt = 0;
@@ -199,6 +200,37 @@ __device__ __forceinline__ void wait_tiles_ahead(int ahead) {
   wait_vmcnt<0>();
 }
 
+// Group i of XCD x's queue under the XCD-aware order xcd_remap<CH> (the
+// groups that order places on XCD x, in the same order), or -1 past its end.
+template <int CH>
+__device__ __forceinline__ int xcd_queue_group(int x, int i, int G) {
+  const int rounds = G / (8 * CH);
+  if (i < rounds * CH) return (i / CH) * (8 * CH) + x * CH + (i % CH);
+  const int g = rounds * 8 * CH + 8 * (i - rounds * CH) + x;
+  return g < G ? g : -1;
+}
+
+// Next group for a persistent workgroup on XCD x: its own XCD's queue first,
+// then the other queues in turn; -1 once every queue is empty.  sched[0..7]
+// count the groups taken from each queue (zeroed before the launch).
+template <int CH>
+__device__ __forceinline__ int grab_group(int* sched, int x, int G) {
+#pragma unroll 1
+  for (int t = 0; t < 8; ++t) {
+    const int y = (x + t) & 7;
+    // skip a queue seen empty without taking a ticket from it
+    if (xcd_queue_group<CH>(y, __hip_atomic_load(&sched[y], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT), G) < 0)
+      continue;
+    const int g = xcd_queue_group<CH>(y, atomicAdd(&sched[y], 1), G);
+    if (g >= 0) return g;
+  }
+  return -1;
+}
+
+__global__ void reset_sched(int* sched) {
+  if (threadIdx.x < 8) sched[threadIdx.x] = 0;
+}
+
 template <int D, bool SPARSE, bool FP8, int QB, int ST, bool TAY = false>
 __global__ __launch_bounds__(128 * QB, QB == 2 ? 2 : 1) void attn_kernel(AttnArgs a) {
   using C = Cfg<D>;
@@ -229,13 +261,33 @@ __global__ __launch_bounds__(128 * QB, QB == 2 ? 2 : 1) void attn_kernel(AttnArg
   // rows of D bf16, unswizzled (operands are gathered from it per element)
   __shared__ __attribute__((aligned(16))) uint8_t vps[TAY ? QB * C::KTILE : 1];
 
-  const int N = a.N, Nb = a.Nb;
+  __shared__ int next_tile_s;
+
+  const int G = a.BH * ((a.Nb + QB - 1) / QB);
+  // Dense: one group per workgroup, XCD-aware order.  Sparse: groups differ
+  // in cost, so a persistent grid takes them from the per-XCD queues (each
+  // XCD's queue holds the groups the XCD-aware order gives it) and, once its
+  // own queue is empty, from the other XCDs' queues.
+  int tile_next = SPARSE ? -1 : xcd_remap<SA_XCD_CHUNK>((int)blockIdx.x, G);
+  for (;;) {
+  if constexpr (SPARSE) {
+    if (threadIdx.x == 0) next_tile_s = grab_group<SA_XCD_CHUNK_SPARSE>(a.sched, (int)blockIdx.x & 7, G);
+    __syncthreads();
+    tile_next = next_tile_s;
+  }
+  const int tile = tile_next;
+  if (tile < 0) break;
+  // The thread index and the sizes pass through empty asm statements, so
+  // that nothing derived from them is hoisted out of the group loop: kept
+  // live across every group, those values would crowd the registers of the
+  // tile loop.
+  int tid_opaque = threadIdx.x, N_opaque = a.N, Nb_opaque = a.Nb;
+  asm volatile("" : "+v"(tid_opaque), "+s"(N_opaque), "+s"(Nb_opaque));
+  const int N = N_opaque, Nb = Nb_opaque;
   const int ngroups = (Nb + QB - 1) / QB;
-  const int G = a.BH * ngroups;
-  const int tile = xcd_remap<SPARSE ? SA_XCD_CHUNK_SPARSE : SA_XCD_CHUNK>((int)blockIdx.x, G);
   const int bh = tile / ngroups;
   const int grp = tile - bh * ngroups;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = tid_opaque, wave = tid >> 6, lane = tid & 63;
   const int qsel = wave >> 1, qhalf = wave & 1;
   const int h = lane >> 5, l32 = lane & 31;
   const int I = QB * grp + qsel;
@@ -253,13 +305,13 @@ __global__ __launch_bounds__(128 * QB, QB == 2 ? 2 : 1) void attn_kernel(AttnArg
     }
     __syncthreads();
     float* p = reinterpret_cast<float*>(smem);
-    proxy_rows<D, NT, QB>(qb, a.kbar + (size_t)bh * Nb * D, Nb, a.scale, nrows, p);
+    proxy_rows<D, NT, QB>(qb, a.kbar + (size_t)bh * Nb * D, Nb, a.scale, nrows, p, tid);
     __syncthreads();
     if (a.topk > 0)
-      topk_rows<NT, QB>(p, Nb, nrows, a.topk, flags, hist, sel, redi, counts);
+      topk_rows<NT, QB>(p, Nb, nrows, a.topk, flags, hist, sel, redi, counts, tid);
     else
-      threshold_rows<NT, QB>(p, Nb, nrows, a.tau, flags, redf, redi, counts);
-    build_union<NT>(flags, Nb, ulist, &nunion_s, redi);
+      threshold_rows<NT, QB>(p, Nb, nrows, a.tau, flags, redf, redi, counts, tid);
+    build_union<NT>(flags, Nb, ulist, &nunion_s, redi, tid);
     nunion = nunion_s;
     if (a.kept && tid < nrows) a.kept[(size_t)bh * Nb + QB * grp + tid] = counts[tid];
     if (a.correction) {
@@ -709,6 +761,10 @@ __global__ __launch_bounds__(128 * QB, QB == 2 ? 2 : 1) void attn_kernel(AttnArg
     }
     if (h == 0) a.lse[qtok] = (m_run + __log2f(lt)) * kLn2;
   }
+  if constexpr (!SPARSE) break;
+  // every wave is done with the group's LDS before the next one is taken
+  __syncthreads();
+  }
 }
 
 #ifndef SA_QB
@@ -718,6 +774,20 @@ __global__ __launch_bounds__(128 * QB, QB == 2 ? 2 : 1) void attn_kernel(AttnArg
 #define SA_STAGES 2
 #endif
 
+// Persistent workgroups for the sparse kernel: as many as the device keeps
+// resident at once (one per compute unit, two at D = 64).
+int resident_groups(int per_cu) {
+  static int ncu[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256 * per_cu;
+  if (ncu[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    ncu[dev] = n;
+  }
+  return ncu[dev] * per_cu;
+}
+
 template <int D, bool FP8>
 hipError_t launch_d(const AttnArgs& a, hipStream_t st) {
   // D = 64 tiles are half the size: two query blocks per workgroup keep at
@@ -725,15 +795,17 @@ hipError_t launch_d(const AttnArgs& a, hipStream_t st) {
   constexpr int QB = D == 64 ? 2 : SA_QB;
   constexpr int STG = SA_STAGES;
   const int ngroups = (a.Nb + QB - 1) / QB;
-  const dim3 grid((unsigned)(a.BH * ngroups));
-  if (a.sparse && a.vprime) {
-    hipLaunchKernelGGL((attn_kernel<D, true, FP8, QB, STG, true>), grid, dim3(128 * QB), 0, st, a);
+  const int G = a.BH * ngroups;
+  if (!a.sparse) {
+    hipLaunchKernelGGL((attn_kernel<D, false, FP8, QB, STG>), dim3((unsigned)G), dim3(128 * QB), 0, st, a);
     return hipGetLastError();
   }
-  if (a.sparse)
-    hipLaunchKernelGGL((attn_kernel<D, true, FP8, QB, STG>), grid, dim3(128 * QB), 0, st, a);
+  hipLaunchKernelGGL(reset_sched, dim3(1), dim3(64), 0, st, a.sched);
+  const dim3 grid((unsigned)std::min(G, resident_groups(QB == 2 ? 2 : 1)));
+  if (a.vprime)
+    hipLaunchKernelGGL((attn_kernel<D, true, FP8, QB, STG, true>), grid, dim3(128 * QB), 0, st, a);
   else
-    hipLaunchKernelGGL((attn_kernel<D, false, FP8, QB, STG>), grid, dim3(128 * QB), 0, st, a);
+    hipLaunchKernelGGL((attn_kernel<D, true, FP8, QB, STG>), grid, dim3(128 * QB), 0, st, a);
   return hipGetLastError();
 }
 

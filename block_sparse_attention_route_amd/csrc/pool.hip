@@ -362,6 +362,10 @@ __global__ __launch_bounds__(256) void pool_kernel(PoolArgs a) {
   __shared__ float part[4096];  // up to 64 row groups x 64 dims or 32 x 128
   __shared__ __attribute__((aligned(16))) uint16_t vtl[D * kBlock];
   const int J = blockIdx.x;
+  // the attention kernel's group counters start zeroed (its launcher zeroes
+  // them again before every launch), so the pool leaves no byte of the
+  // workspace undefined
+  if (!VT_ONLY && a.sched && blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x < 64) a.sched[threadIdx.x] = 0;
   if constexpr (PRO) {
     RopeRows<D, Tiling<ELT_BF16, D>::P> ang;
     rope_rows<D>(J * kBlock, min(kBlock, a.N - J * kBlock), a.tm, a.pro, ang);

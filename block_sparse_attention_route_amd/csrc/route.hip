@@ -37,12 +37,12 @@ __global__ __launch_bounds__(256) void route_kernel(RouteArgs a) {
     qb[tid] = (I < a.Nb) ? a.qbar[((size_t)bh * a.Nb + I) * D + d] : 0.f;
   }
   __syncthreads();
-  proxy_rows<D, 256, 2>(qb, a.kbar + (size_t)bh * a.Nb * D, a.Nb, a.scale, two ? 2 : 1, p);
+  proxy_rows<D, 256, 2>(qb, a.kbar + (size_t)bh * a.Nb * D, a.Nb, a.scale, two ? 2 : 1, p, tid);
   __syncthreads();
   if (a.topk > 0)
-    topk_rows<256, 2>(p, a.Nb, two ? 2 : 1, a.topk, flags, hist, sel, redi, counts);
+    topk_rows<256, 2>(p, a.Nb, two ? 2 : 1, a.topk, flags, hist, sel, redi, counts, tid);
   else
-    threshold_rows<256, 2>(p, a.Nb, two ? 2 : 1, a.tau, flags, redf, redi, counts);
+    threshold_rows<256, 2>(p, a.Nb, two ? 2 : 1, a.tau, flags, redf, redi, counts, tid);
 
   uint8_t* m0 = a.mask + ((size_t)bh * a.Nb + I0) * a.Nb;
   for (int J = tid; J < a.Nb; J += 256) {

@@ -114,14 +114,14 @@ __device__ __forceinline__ int wave_sum_int(int x) {
 // routine, obtain identical bits.
 //
 // qbar: LDS [QB][D] (rows >= nrows ignored).  kbar: global [Nb][D].
-// p: LDS [QB][Nb] output, complete after a barrier.
+// p: LDS [QB][Nb] output, complete after a barrier.  tid: the thread index
+// in the workgroup (as do the routines below).
 // ---------------------------------------------------------------------------
 template <int D, int NTHREADS, int QB>
 __device__ __forceinline__ void proxy_rows(const float* __restrict__ qbar,
                                            const float* __restrict__ kbar, int Nb, float scale,
-                                           int nrows, float* __restrict__ p) {
+                                           int nrows, float* __restrict__ p, int tid) {
   constexpr int DPL = D / 16;  // dims per lane
-  const int tid = threadIdx.x;
   const int sub = tid & 15;
   const int slot = tid >> 4;
   constexpr int ROWS_PER_PASS = NTHREADS / 16;
@@ -175,9 +175,8 @@ template <int NTHREADS, int QB>
 __device__ __forceinline__ void threshold_rows(const float* __restrict__ p, int Nb, int nrows,
                                                float tau, uint8_t* __restrict__ flags,
                                                float* __restrict__ redf, int* __restrict__ redi,
-                                               int* __restrict__ counts) {
+                                               int* __restrict__ counts, int tid) {
   constexpr int NW = NTHREADS / 64;
-  const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
   float m[QB];
 #pragma unroll
@@ -251,10 +250,10 @@ template <int NTHREADS, int QB>
 __device__ __forceinline__ void topk_rows(const float* __restrict__ p, int Nb, int nrows, int topk,
                                           uint8_t* __restrict__ flags, int* __restrict__ hist,
                                           uint32_t* __restrict__ sel, int* __restrict__ wsum,
-                                          int* __restrict__ counts) {
+                                          int* __restrict__ counts, int tid) {
   constexpr int NW = NTHREADS / 64;
   static_assert(NW >= QB, "one wave per row for the digit search");
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int wave = tid >> 6, lane = tid & 63;
   const int kk = min(topk, Nb);
   uint32_t* prefix = sel;            // [QB] key bits fixed so far
   uint32_t* need = sel + QB;         // [QB] blocks still to take among those matching prefix

@@ -42,6 +42,7 @@ struct PoolArgs {
   TileMap tm;            // position -> token order (on == 0: raster)
   uint16_t* kpos16;      // K in position order, written when tm.on (bf16 K)
   ProArgs pro;           // producer step fused in front (pro.on)
+  int* sched;            // the attention kernel's group counters [64], zeroed here (or null)
 };
 
 // First-order values of the skipped blocks (correction mode 2): the bf16
@@ -99,6 +100,7 @@ struct AttnArgs {
   bool sparse;           // false: dense attention over all blocks
   const uint16_t* vprime;  // correction mode 2: first-order values, else null
   const float* vprime32;   // the same for the float32 path
+  int* sched;              // sparse: 8 per-XCD group counters (zeroed by the launcher)
 };
 
 hipError_t launch_pool(const PoolArgs& a, hipStream_t st);

@@ -11,6 +11,8 @@
 //                                     transposed (d-major), keys >= N zero (bf16 V only)
 //   kpos16  bf16  [BH][N][D]          K in block (position) order; only with a
 //                                     3-D tile order (bf16 K only)
+//   sched   int   [64]                group counters of the sparse attention
+//                                     kernel's persistent workgroups
 //   vprime  bf16  [BH][Nb][Nbp][D]    first-order values of the skipped blocks,
 //                                     per query block I and key block J, rows
 //                                     J >= Nb zero; only with correction mode 2
@@ -29,7 +31,7 @@ constexpr int kBlock = 64;
 constexpr int kMaxNb = 4096;
 
 struct WsLayout {
-  size_t qbar, kbar, vbar, kbar16, vbarT16, vt16, kpos16, vprime, total;
+  size_t qbar, kbar, vbar, kbar16, vbarT16, vt16, kpos16, sched, vprime, total;
 };
 
 // Position -> token map of the 3-D tile order.  Full tiles of tt x th x tw =
@@ -116,6 +118,7 @@ __host__ __device__ inline WsLayout ws_layout(int64_t BH, int64_t N, int64_t D, 
   }
   if (v_bf16) L.vt16 = take((size_t)(BH * Nb * D * kBlock) * 2);
   if (tiled && v_bf16 && !dense_only) L.kpos16 = take((size_t)(BH * N * D) * 2);
+  if (!dense_only) L.sched = take(256);
   if (first_order && !dense_only)
     L.vprime = v_bf16 ? take((size_t)BH * Nb * Nbp * D * 2) : take((size_t)BH * Nb * Nb * D * 4);
   L.total = off;

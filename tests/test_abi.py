@@ -67,11 +67,12 @@ def test_workspace_bytes_layout(lib):
 
     def a256(x):
         return (x + 255) // 256 * 256
-    expect = 3 * a256(BH * Nb * D * 4) + 2 * a256(BH * Nbp * D * 2) + a256(BH * Nb * D * 64 * 2)
+    # means, bf16 mean copies, V regrouped, 256 bytes of group counters
+    expect = 3 * a256(BH * Nb * D * 4) + 2 * a256(BH * Nbp * D * 2) + a256(BH * Nb * D * 64 * 2) + 256
     assert n == expect
-    # fp32 path keeps only the fp32 means
+    # fp32 path keeps only the fp32 means (and the counters)
     n32 = lib.sa_workspace_bytes(ctypes.byref(sh), None, ctypes.byref(_inputs(api.SA_F32, api.SA_F32)))
-    assert n32 == 3 * a256(BH * Nb * D * 4)
+    assert n32 == 3 * a256(BH * Nb * D * 4) + 256
     nd = lib.sa_dense_workspace_bytes(ctypes.byref(sh), ctypes.byref(_inputs()))
     assert nd == a256(BH * Nb * D * 64 * 2)
     nd32 = lib.sa_dense_workspace_bytes(ctypes.byref(sh), ctypes.byref(_inputs(api.SA_F32, api.SA_F32)))
