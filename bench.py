@@ -21,8 +21,9 @@ the tile_order list times it with blocks formed over 3-D tiles of the token
 grid (4x4x4 and 1x8x8 by default); fused_producer times sa_qk_prologue (norm
 + rotary + pool of the Q/K projections) in place of the pool; first_order
 times the call with the first-order correction of the skipped blocks
-(correction = 2: the pool step also writes the per-pair values, the fused
-kernel reads them) and its error against dense attention.  The configs list
+(correction = 2: the attention call computes the per-pair values a slab of
+heads at a time and the fused kernel reads them) and its error against dense
+attention.  The configs list
 repeats the call (a few steps each) at the other workloads: 720p at tau 4
 and 8, 480p, 1080p and the 720p CFG batch with fp8 Q/K, each with its dense
 call, density, and -- from the CPU leg -- the near-threshold and flipped
@@ -434,8 +435,9 @@ def main() -> None:
         del wsd, o_t, l_t
 
     # first-order correction of the skipped blocks (correction = 2) at the
-    # same tau: the pool step also writes one first-order value per (query
-    # block, key block), and the fused kernel's correction tiles read them
+    # same tau: the attention call computes one first-order value per (query
+    # block, key block) for a slab of heads at a time, then runs the fused
+    # kernel on that slab, whose correction tiles read them
     first_order = None
     if wl.dtype == "bf16" and args.first_order:
         wsf = torch.empty(api.sa_workspace_bytes(q, k, v, grid, correction=2), dtype=torch.uint8, device=dev)
@@ -459,19 +461,13 @@ def main() -> None:
             fstep(fevs[i])
         torch.cuda.synchronize()
         fpool = float(np.mean([e[0].elapsed_time(e[1]) for e in fevs]))
-        ffused = float(np.mean([e[1].elapsed_time(e[2]) for e in fevs]))
-        bh, nbp = wl.B * wl.H, (wl.Nb + 63) // 64 * 64
-        # values kernel: reads K, V (bf16) and the fp32 means, writes the
-        # bf16 values; 4*64*D flops per (query block, key block) pair
-        vbytes = bh * wl.N * wl.D * 2 * 2 + 3 * bh * wl.Nb * wl.D * 4 + bh * wl.Nb * nbp * wl.D * 2
-        vflops = 4.0 * 64 * wl.D * bh * wl.Nb * wl.Nb
-        vms = fpool - pool_avg
-        first_order = {"tau": tau, "ms": fpool + ffused, "pool_and_values_ms": fpool,
-                       "values_ms_by_difference": vms, "fused_kernel_ms": ffused,
-                       "values_bytes": vbytes, "values_gbs": vbytes / (vms * 1e-3) / 1e9,
-                       "values_tflops": vflops / (vms * 1e-3) / 1e12,
+        fattn = float(np.mean([e[1].elapsed_time(e[2]) for e in fevs]))
+        first_order = {"tau": tau, "ms": fpool + fattn, "pool_ms": fpool,
+                       "values_and_fused_kernel_ms": fattn,
+                       "values_by_difference_ms": fattn - fused_avg,
                        "workspace_gib": wsf.numel() / 2 ** 30,
-                       "time_vs_mean_copies": (fpool + ffused) / ms_step,
+                       "heads_per_slab": api.first_order_slab(q, v),
+                       "time_vs_mean_copies": (fpool + fattn) / ms_step,
                        "approx_vs_dense": approx_vs(of, lsef, od, lsed) if od is not None else None}
         del wsf
         if od is not None:
@@ -483,7 +479,7 @@ def main() -> None:
                 torch.cuda.synchronize()
                 tiled_err[name] = approx_vs(of, lsef, od, lsed)
             first_order["approx_vs_dense_tiled"] = tiled_err
-        log(f"first-order correction: pool+values {fpool:.2f} ms, fused {ffused:.2f} ms")
+        log(f"first-order correction: pool {fpool:.2f} ms, values + fused {fattn:.2f} ms")
         del of, lsef
     del od, lsed
 

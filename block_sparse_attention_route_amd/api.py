@@ -18,7 +18,7 @@ __all__ = [
     "SaError", "load_library", "library_path", "Shape", "Params", "Inputs",
     "sa_abi_version", "sa_workspace_bytes", "sa_dense_workspace_bytes", "sa_pool", "sa_route",
     "sa_forward", "sa_forward_pooled", "sa_dense_forward", "sa_qk_prologue", "status_name",
-    "Prologue", "make_params", "budget_blocks",
+    "Prologue", "make_params", "budget_blocks", "first_order_slab",
     "SA_F32", "SA_BF16", "SA_FP8_E4M3", "BLOCK", "MAX_NB", "MAX_N",
 ]
 
@@ -94,6 +94,10 @@ def load_library():
     lib.sa_workspace_bytes.argtypes = [P, S, I]
     lib.sa_dense_workspace_bytes.restype = sz
     lib.sa_dense_workspace_bytes.argtypes = [P, I]
+    lib.sa_first_order_slab_heads.restype = ctypes.c_int64
+    lib.sa_first_order_slab_heads.argtypes = [P, I]
+    lib.sa_budget_blocks.restype = ctypes.c_int32
+    lib.sa_budget_blocks.argtypes = [ctypes.c_int32, ctypes.c_double]
     lib.sa_pool.restype = st
     lib.sa_pool.argtypes = [P, S, I, vp, sz, vp]
     lib.sa_route.restype = st
@@ -143,17 +147,29 @@ def make_shape(q: torch.Tensor, grid) -> Shape:
 def make_params(tau: float, correction=True, scale: float = 0.0, topk: int = 0,
                 tile=None) -> Params:
     """correction: False / 0 none, True / 1 the mean copies, 2 the first-order
-    correction (bf16 inputs)."""
+    correction (every dtype pair)."""
     tt, th, tw = (0, 0, 0) if tile is None else (int(x) for x in tile)
     return Params(BLOCK, float(tau), int(correction), float(scale), int(topk), tt, th, tw)
 
 
 def budget_blocks(sparsity: float, N: int) -> int:
     """Key blocks kept per query block at a fixed sparsity (fraction of the
-    Nb key blocks skipped): ceil((1 - sparsity) * Nb), at least 1."""
-    if not 0.0 <= sparsity < 1.0:
-        raise ValueError("sparsity must be in [0, 1)")
-    return max(1, math.ceil((1.0 - sparsity) * _nb(N) - 1e-9))
+    Nb key blocks skipped): ceil((1 - sparsity) * Nb), at least 1 (the
+    library's sa_budget_blocks)."""
+    lib = load_library()
+    n = int(lib.sa_budget_blocks(int(N), float(sparsity)))
+    if n == 0:
+        raise ValueError(lib.sa_last_error().decode())
+    return n
+
+
+def first_order_slab(q, v) -> int:
+    """Heads per slab of the first-order correction (sa_first_order_slab_heads)."""
+    lib = load_library()
+    B, H, N, D = q.shape
+    sh = Shape(B, H, N, D, 1, 1, N)
+    inp = Inputs(None, None, None, None, None, _dtype_code(q), _dtype_code(v))
+    return int(lib.sa_first_order_slab_heads(ctypes.byref(sh), ctypes.byref(inp)))
 
 
 def make_inputs(q, k, v, q_scale=None, k_scale=None) -> Inputs:
@@ -200,7 +216,7 @@ def sa_pool(q, k, v, grid, *, tau: float = math.inf, correction=True, scale: flo
             workspace: torch.Tensor | None = None, q_scale=None, k_scale=None, topk: int = 0,
             tile=None) -> torch.Tensor:
     """Step pool: block means (and V regrouped per 64-key block) into the
-    workspace; with correction=2 also the first-order values."""
+    workspace."""
     lib = load_library()
     ws = _workspace(sa_workspace_bytes(q, k, v, grid, q_scale, k_scale, tile, correction), q, workspace)
     sh, pr, inp = make_shape(q, grid), make_params(tau, correction, scale, topk, tile), make_inputs(q, k, v, q_scale, k_scale)

@@ -4,6 +4,7 @@
 // message in a thread-local buffer.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -196,6 +197,7 @@ sa::AttnArgs attn_args(const Req& r, const sa_inputs* in, void* o, float* lse, i
     a.vbar = at<float>(ws, r.ws.vbar);
     if (r.v == SA_BF16) {
       a.kbar16 = at<uint16_t>(ws, r.ws.kbar16);
+      a.kbarlo16 = a.kbar16 + (size_t)r.BH * r.Nbp * r.D;
       a.vbarT16 = at<uint16_t>(ws, r.ws.vbarT16);
     }
   }
@@ -234,32 +236,34 @@ sa_status hip_status(hipError_t e, const char* what) {
   return ok();
 }
 
-// The first-order correction's values per (query block, key block), from the
-// pooled means in the workspace and K (bf16: its position-order copy with a
-// 3-D tile order, V from the regrouped copy; fp32: K and V read through the
-// order).
+// The first-order correction's values per (query block, key block) of heads
+// [bh0, bh0 + nbh), from the pooled means in the workspace and K (bf16: its
+// position-order copy with a 3-D tile order, V from the regrouped copy; fp32:
+// K and V read through the order), into the workspace's slab of values.
 sa_status run_taylor(const Req& r, const void* k, const void* v, const float* k_scale, void* ws,
-                     hipStream_t st) {
+                     int64_t bh0, int64_t nbh, hipStream_t st) {
   sa::TaylorArgs a{};
-  a.qbar = at<float>(ws, r.ws.qbar);
-  a.kbar = at<float>(ws, r.ws.kbar);
-  a.vbar = at<float>(ws, r.ws.vbar);
+  const size_t mh = (size_t)bh0 * r.Nb * r.D;  // per-head offsets of the inputs
+  const size_t th = (size_t)bh0 * r.N * r.D;
+  a.qbar = at<float>(ws, r.ws.qbar) + mh;
+  a.kbar = at<float>(ws, r.ws.kbar) + mh;
+  a.vbar = at<float>(ws, r.ws.vbar) + mh;
   if (r.qk == SA_F32) {
-    a.kf = static_cast<const float*>(k);
-    a.vf = static_cast<const float*>(v);
+    a.kf = static_cast<const float*>(k) + th;
+    a.vf = static_cast<const float*>(v) + th;
     a.tm = r.tm;
     a.vprime32 = at<float>(ws, r.ws.vprime);
   } else {
     if (r.qk == SA_FP8_E4M3) {
-      a.k8 = static_cast<const uint8_t*>(k);   // fp8 Q/K have no 3-D tile order
-      a.k_scale = k_scale;
+      a.k8 = static_cast<const uint8_t*>(k) + th;   // fp8 Q/K have no 3-D tile order
+      a.k_scale = k_scale + (size_t)bh0 * r.Nb;
     } else {
-      a.k = static_cast<const uint16_t*>(r.tm.on ? at<uint16_t>(ws, r.ws.kpos16) : k);
+      a.k = static_cast<const uint16_t*>(r.tm.on ? at<uint16_t>(ws, r.ws.kpos16) : k) + th;
     }
-    a.vt16 = at<uint16_t>(ws, r.ws.vt16);
+    a.vt16 = at<uint16_t>(ws, r.ws.vt16) + (size_t)bh0 * r.Nb * r.D * SA_BLOCK;
     a.vprime = at<uint16_t>(ws, r.ws.vprime);
   }
-  a.BH = (int)r.BH;
+  a.BH = (int)nbh;
   a.N = (int)r.N;
   a.Nb = (int)r.Nb;
   a.Nbp = (int)r.Nbp;
@@ -268,19 +272,55 @@ sa_status run_taylor(const Req& r, const void* k, const void* v, const float* k_
   return hip_status(sa::launch_taylor(a, st), "first-order values kernel launch");
 }
 
-// Pool step, followed by the first-order values when that correction is on.
 sa_status run_pool(const Req& r, const sa_inputs* in, void* ws, hipStream_t st) {
-  sa_status s;
-  if ((s = hip_status(sa::launch_pool(pool_args(r, in, ws, false), st), "pool kernel launch")) != SA_OK)
-    return s;
-  return r.correction == 2 ? run_taylor(r, in->k, in->v, in->k_scale, ws, st) : s;
+  return hip_status(sa::launch_pool(pool_args(r, in, ws, false), st), "pool kernel launch");
+}
+
+// The arguments of one launch over heads [bh0, bh0 + nbh): every per-head
+// tensor pointer moves to head bh0; the first-order values are slab-local.
+sa::AttnArgs head_slab(sa::AttnArgs a, const Req& r, int64_t bh0, int64_t nbh) {
+  const size_t nd = (size_t)bh0 * r.N * r.D, bd = (size_t)bh0 * r.Nb * r.D, pd = (size_t)bh0 * r.Nbp * r.D;
+  const size_t qe = r.qk == SA_F32 ? 4 : r.qk == SA_BF16 ? 2 : 1, ve = r.v == SA_F32 ? 4 : 2;
+  auto adv = [](const void* p, size_t bytes) -> const void* {
+    return p ? static_cast<const uint8_t*>(p) + bytes : nullptr;
+  };
+  a.q = adv(a.q, nd * qe);
+  a.k = adv(a.k, nd * qe);
+  a.v = adv(a.v, nd * ve);
+  if (a.q_scale) a.q_scale += (size_t)bh0 * r.Nb;
+  if (a.k_scale) a.k_scale += (size_t)bh0 * r.Nb;
+  if (a.qbar) a.qbar += bd;
+  if (a.kbar) a.kbar += bd;
+  if (a.vbar) a.vbar += bd;
+  if (a.kbar16) a.kbar16 += pd;
+  if (a.kbarlo16) a.kbarlo16 += pd;
+  if (a.vbarT16) a.vbarT16 += pd;
+  if (a.vt16) a.vt16 += bd * SA_BLOCK;
+  if (a.kpos16) a.kpos16 += nd;
+  a.o = static_cast<uint8_t*>(a.o) + nd * ve;
+  a.lse += (size_t)bh0 * r.N;
+  if (a.kept) a.kept += (size_t)bh0 * r.Nb;
+  a.BH = (int)nbh;
+  return a;
 }
 
 sa_status run_attn(const Req& r, const sa_inputs* in, void* o, float* lse, int32_t* kept, void* ws,
                    bool sparse, hipStream_t st) {
   const sa::AttnArgs a = attn_args(r, in, o, lse, kept, ws, sparse);
-  const hipError_t e = (r.qk == SA_F32) ? sa::launch_attn_f32(a, st) : sa::launch_attn_mfma(a, st);
-  return hip_status(e, "attention kernel launch");
+  auto launch = [&](const sa::AttnArgs& x) {
+    return hip_status(r.qk == SA_F32 ? sa::launch_attn_f32(x, st) : sa::launch_attn_mfma(x, st),
+                      "attention kernel launch");
+  };
+  if (!(sparse && r.correction == 2)) return launch(a);
+  // first-order correction: per slab of heads, the values, then the attention
+  const int64_t slab = sa::first_order_slab(r.BH, r.N, r.D, r.v == SA_BF16);
+  for (int64_t bh0 = 0; bh0 < r.BH; bh0 += slab) {
+    const int64_t nbh = std::min<int64_t>(slab, r.BH - bh0);
+    sa_status s = run_taylor(r, in->k, in->v, in->k_scale, ws, bh0, nbh, st);
+    if (s != SA_OK) return s;
+    if ((s = launch(head_slab(a, r, bh0, nbh))) != SA_OK) return s;
+  }
+  return ok();
 }
 
 }  // namespace
@@ -314,6 +354,25 @@ SA_API size_t sa_workspace_bytes(const sa_shape* shape, const sa_params* params,
   }
   ok();
   return r.ws.total;
+}
+
+SA_API int64_t sa_first_order_slab_heads(const sa_shape* shape, const sa_inputs* in) {
+  Req r{};
+  if (check_shape_inputs(shape, in, &r, false, false) != SA_OK) return 0;
+  ok();
+  return r.BH == 0 ? 0 : sa::first_order_slab(r.BH, r.N, r.D, r.v == SA_BF16);
+}
+
+SA_API int32_t sa_budget_blocks(int32_t N, double sparsity) {
+  if (N < 1 || !(sparsity >= 0.0) || !(sparsity < 1.0)) {
+    fail(SA_ERR_PARAM, "budget needs N >= 1 and sparsity in [0, 1)");
+    return 0;
+  }
+  ok();
+  const int64_t Nb = ((int64_t)N + SA_BLOCK - 1) / SA_BLOCK;
+  // the 1e-9 keeps a product that is an integer up to rounding at that integer
+  const int64_t k = (int64_t)std::ceil((1.0 - sparsity) * (double)Nb - 1e-9);
+  return (int32_t)std::max<int64_t>(1, std::min<int64_t>(k, Nb));
 }
 
 SA_API size_t sa_dense_workspace_bytes(const sa_shape* shape, const sa_inputs* in) {
@@ -418,8 +477,7 @@ SA_API sa_status sa_qk_prologue(const sa_shape* shape, const sa_params* params, 
   a.pro.T = r.T;
   a.pro.Hg = r.Hg;
   a.pro.Wg = r.Wg;
-  if ((s = hip_status(sa::launch_pool(a, (hipStream_t)stream), "producer kernel launch")) != SA_OK) return s;
-  return r.correction == 2 ? run_taylor(r, k_out, in->v, nullptr, ws, (hipStream_t)stream) : s;
+  return hip_status(sa::launch_pool(a, (hipStream_t)stream), "producer kernel launch");
 }
 
 SA_API sa_status sa_dense_forward(const sa_shape* shape, float scale, const sa_inputs* in, void* o,

@@ -130,7 +130,6 @@ struct Cfg {
   static constexpr int CPR8 = KROW8 / 16;
   static constexpr int KTILE = 64 * KROW16;  // K buffer bytes (sized for bf16)
   static constexpr int VTILE = D * 128;      // V^T tile: D rows of 64 bf16 keys
-  static constexpr int STAGE = KTILE + VTILE;
 };
 
 // 16 bytes per lane from global memory straight into LDS (LDS DMA): lane l's
@@ -240,7 +239,13 @@ __global__ __launch_bounds__(128 * QB, QB == 2 ? 2 : 1) void attn_kernel(AttnArg
   constexpr int KI8 = C::KTILE / 2 / 1024 / NW;    // fp8 K tile
   constexpr int VI = C::VTILE / 1024 / NW;         // V^T tile
   constexpr int LPT = (FP8 ? (KI8 < KI16 ? KI8 : KI16) : KI16) + VI;  // fewest copies per tile
-  constexpr int SMEM_STAGE = ST * C::STAGE;
+  // A ring stage holds a K tile and a V^T tile.  Correction tiles take the
+  // key means in two bf16 halves: the low half goes to a third buffer of the
+  // stage, or, with first-order values (whose PV operand comes from its own
+  // LDS area), to the V^T buffer.
+  constexpr int STAGE = C::KTILE + C::VTILE + ((SPARSE && !TAY) ? C::KTILE : 0);
+  constexpr int LO_OFF = TAY ? C::KTILE : C::KTILE + C::VTILE;
+  constexpr int SMEM_STAGE = ST * STAGE;
   constexpr int SMEM_PROXY = SPARSE ? QB * kMaxNb * 4 : 0;
   constexpr int SMEM = SMEM_STAGE > SMEM_PROXY ? SMEM_STAGE : SMEM_PROXY;
   static_assert(KI8 >= 1 && VI >= 1, "tile copies per wave");
@@ -401,24 +406,32 @@ __global__ __launch_bounds__(128 * QB, QB == 2 ? 2 : 1) void attn_kernel(AttnArg
   // logical chunk pc ^ swz(r).  Rows past the end of the sequence re-read the
   // last valid row (finite data; those keys are masked).
   auto issue_tile = [&](int it, int stg) {
-    const uint8_t* ksrc;
-    const uint8_t* vsrc;
-    int kvalid = 64;
-    bool k8 = false;
-    if (it < nvirt) {
-      ksrc = reinterpret_cast<const uint8_t*>(a.kbar16 + ((size_t)bh * a.Nbp + 64 * it) * D);
-      vsrc = reinterpret_cast<const uint8_t*>(a.vbarT16 + ((size_t)bh * (a.Nbp / 64) + it) * D * 64);
-    } else {
-      const int J = __builtin_amdgcn_readfirstlane(tile_block(it));
-      k8 = FP8;
-      // keys in position order: the caller's K, or its copy in tile order
-      const void* kpos = (!FP8 && a.tm.on) ? static_cast<const void*>(a.kpos16) : a.k;
-      ksrc = reinterpret_cast<const uint8_t*>(kpos) + ((size_t)bh * N + (size_t)J * kBlock) * D * (FP8 ? 1 : 2);
-      vsrc = reinterpret_cast<const uint8_t*>(a.vt16 + ((size_t)bh * Nb + J) * D * kBlock);
-      kvalid = min(kBlock, N - J * kBlock);
-    }
-    const uint32_t kb = smem_base + stg * C::STAGE;
+    const uint32_t kb = smem_base + stg * STAGE;
     const uint32_t vb = kb + C::KTILE;
+    if (it < nvirt) {
+      // 64 virtual keys: both bf16 halves of their key means (rows >= Nb
+      // are zero) and, for the mean copies, the transposed value means
+      const size_t row0 = ((size_t)bh * a.Nbp + 64 * it) * D;
+      const uint64_t hbase = uniform_addr(a.kbar16 + row0), lbase = uniform_addr(a.kbarlo16 + row0);
+#pragma unroll
+      for (int i = 0; i < KI16; ++i) dma16s(koff[i], hbase, kb + (wave + NW * i) * 1024);
+#pragma unroll
+      for (int i = 0; i < KI16; ++i) dma16s(koff[i], lbase, kb + LO_OFF + (wave + NW * i) * 1024);
+      if constexpr (!TAY) {
+        const uint64_t vbase = uniform_addr(a.vbarT16 + ((size_t)bh * (a.Nbp / 64) + it) * D * 64);
+#pragma unroll
+        for (int i = 0; i < VI; ++i) dma16s(voff[i], vbase, vb + (wave + NW * i) * 1024);
+      }
+      return;
+    }
+    const int J = __builtin_amdgcn_readfirstlane(tile_block(it));
+    constexpr bool k8 = FP8;
+    // keys in position order: the caller's K, or its copy in tile order
+    const void* kpos = (!FP8 && a.tm.on) ? static_cast<const void*>(a.kpos16) : a.k;
+    const uint8_t* ksrc =
+        reinterpret_cast<const uint8_t*>(kpos) + ((size_t)bh * N + (size_t)J * kBlock) * D * (FP8 ? 1 : 2);
+    const uint8_t* vsrc = reinterpret_cast<const uint8_t*>(a.vt16 + ((size_t)bh * Nb + J) * D * kBlock);
+    const int kvalid = min(kBlock, N - J * kBlock);
     if (!k8 && kvalid == kBlock) {
       const uint64_t kbase = uniform_addr(ksrc), vbase = uniform_addr(vsrc);
 #pragma unroll
@@ -530,23 +543,28 @@ __global__ __launch_bounds__(128 * QB, QB == 2 ? 2 : 1) void attn_kernel(AttnArg
     //   region 3: PV of half 1
     // Operands are read from LDS NPRE products ahead, and the source order is
     // pinned with scheduling barriers.
-    const uint8_t* Kb = smem + stg * C::STAGE;
+    const uint8_t* Kb = smem + stg * STAGE;
     const uint8_t* Vb = Kb + C::KTILE;
     float c2 = c2_base * qscale;
     constexpr bool k8 = FP8 && !virt;
     if constexpr (k8) c2 *= scalar_load_f32(a.k_scale + ((size_t)bh * Nb + J));
     constexpr int KS = C::KS, DT = C::DT;
-    // products of S^T per half: D/16 bf16 MFMAs (K = 16), or D/64 fp8 ones
+    // products of S^T per half: D/16 bf16 MFMAs (K = 16); twice as many for
+    // the correction tiles (the high and the low bf16 half of each key mean
+    // against the same bf16 Q, summed in float32); or D/64 fp8 ones
     // (v_mfma_f32_32x32x64_f8f6f4, K = 64, twice the bf16 rate)
-    constexpr int NS = k8 ? D / 64 : KS;
+    constexpr int NS = k8 ? D / 64 : (virt ? 2 * KS : KS);
     constexpr int NPRE = 4;               // V^T operands in flight
     constexpr int NPK = k8 ? 2 : NPRE;    // K operands in flight
-    constexpr int PA = 8 / NS;            // weight pairs per product in region 1
-    constexpr int PB = 8 / (2 * DT);      // and in region 2
+    constexpr int PB = 8 / (2 * DT);      // weight pairs per product in region 2
     using KOp = typename std::conditional<k8, i32x8, bf16x8>::type;
     auto kop = [&](int i) __attribute__((always_inline)) {  // operand of product i of region 1
       const int kt = i / NS, m = i % NS;
       const int krow = 32 * kt + kperm(l32);
+      if constexpr (virt) {
+        const uint8_t* half = Kb + (m < KS ? 0 : LO_OFF);
+        return *reinterpret_cast<const bf16x8*>(half + krow * C::KROW16 + swz<C::CPR16>(krow, 2 * (m % KS) + h) * 16);
+      }
       if constexpr (k8) {
         // 32 codes: dims [64m + 32h, +32) of key row krow, two 16-byte chunks
         const uint8_t* row = Kb + krow * C::KROW8;
@@ -655,7 +673,7 @@ __global__ __launch_bounds__(128 * QB, QB == 2 ? 2 : 1) void attn_kernel(AttnArg
 #pragma unroll
     for (int i = 0; i < 2 * NS; ++i) {
       const int kt = i / NS;
-      mfma_s(kb[i % NPK], i % NS, s[kt]);
+      mfma_s(kb[i % NPK], virt ? (i % NS) % KS : i % NS, s[kt]);
       if (i + NPK < 2 * NS) {
         kb[i % NPK] = kop(i + NPK);
       } else if constexpr (!tv) {
@@ -664,9 +682,10 @@ __global__ __launch_bounds__(128 * QB, QB == 2 ? 2 : 1) void attn_kernel(AttnArg
         for (int v = (i + NPK - 2 * NS) * NPRE / NPK; v < (i + NPK - 2 * NS + 1) * NPRE / NPK; ++v) vb[v] = vop(v);
       }
       if (i >= NS) {
+        // the 8 weight pairs of half 0 spread over the products of half 1
         const float negm = -m_run;
 #pragma unroll
-        for (int p = 0; p < PA; ++p) w_pair(0, 2 * ((i - NS) * PA + p), negm, std::true_type{});
+        for (int p = (i - NS) * 8 / NS; p < (i - NS + 1) * 8 / NS; ++p) w_pair(0, 2 * p, negm, std::true_type{});
       }
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -803,7 +822,8 @@ hipError_t launch_d(const AttnArgs& a, hipStream_t st) {
   hipLaunchKernelGGL(reset_sched, dim3(1), dim3(64), 0, st, a.sched);
   const dim3 grid((unsigned)std::min(G, resident_groups(QB == 2 ? 2 : 1)));
   if (a.vprime)
-    hipLaunchKernelGGL((attn_kernel<D, true, FP8, QB, STG, true>), grid, dim3(128 * QB), 0, st, a);
+    // the first-order value tiles take 64 KB of LDS: two ring stages
+    hipLaunchKernelGGL((attn_kernel<D, true, FP8, QB, 2, true>), grid, dim3(128 * QB), 0, st, a);
   else
     hipLaunchKernelGGL((attn_kernel<D, true, FP8, QB, STG>), grid, dim3(128 * QB), 0, st, a);
   return hipGetLastError();

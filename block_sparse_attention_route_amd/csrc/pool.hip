@@ -104,10 +104,13 @@ __device__ __forceinline__ void thread_sums(const u32x4 (&raw)[Tiling<E, D>::P],
 
 // Per-thread sums -> mean over rows in out[0..D) (fp32), scaled by mult; the
 // row groups' partial sums are added in order through part[G][D] in LDS.
+// With out_bf16, the mean also goes out as two bf16 halves: hi = bf16(m) at
+// out_bf16[d] and lo = bf16(m - hi) at out_bf16[lo_off + d] (hi + lo carries
+// about 16 significant bits).
 template <int E, int D>
 __device__ __forceinline__ void mean_finish(const float (&acc)[Tiling<E, D>::EPC], int nrows, float mult,
                                             float* __restrict__ part, float* __restrict__ out_f32,
-                                            uint16_t* __restrict__ out_bf16) {
+                                            uint16_t* __restrict__ out_bf16, size_t lo_off = 0) {
   using T = Tiling<E, D>;
   const int c = threadIdx.x % T::CPR, g = threadIdx.x / T::CPR;
 #pragma unroll
@@ -120,7 +123,11 @@ __device__ __forceinline__ void mean_finish(const float (&acc)[Tiling<E, D>::EPC
     for (int gg = 0; gg < T::G; ++gg) s += part[gg * D + d];
     const float m = (s / (float)nrows) * mult;
     out_f32[d] = m;
-    if (out_bf16) out_bf16[d] = f32_to_bf16_bits(m);
+    if (out_bf16) {
+      const uint16_t hi = f32_to_bf16_bits(m);
+      out_bf16[d] = hi;
+      out_bf16[lo_off + d] = f32_to_bf16_bits(m - bf16_bits_to_f32(hi));
+    }
   }
   __syncthreads();
 }
@@ -130,10 +137,10 @@ template <int E, int D>
 __device__ __forceinline__ void block_mean(const u32x4 (&raw)[Tiling<E, D>::P], int nrows,
                                            float mult, float* __restrict__ part,
                                            float* __restrict__ out_f32,
-                                           uint16_t* __restrict__ out_bf16) {
+                                           uint16_t* __restrict__ out_bf16, size_t lo_off = 0) {
   float acc[Tiling<E, D>::EPC];
   thread_sums<E, D>(raw, acc);
-  mean_finish<E, D>(acc, nrows, mult, part, out_f32, out_bf16);
+  mean_finish<E, D>(acc, nrows, mult, part, out_f32, out_bf16, lo_off);
 }
 
 // Rotation angles of this thread's rows: (cos, sin) of pos_a * theta for its
@@ -257,7 +264,8 @@ __device__ __forceinline__ void pool_block(const PoolArgs& a, int J, int bh, flo
         norm_rope<D>(rq, nrows, a.pro.q_gain, a.pro.eps, *ang, a.pro.q_out + head0 * D, acc);
         mean_finish<QE, D>(acc, nrows, 1.f, part, a.qbar + mrow, nullptr);
         norm_rope<D>(rk, nrows, a.pro.k_gain, a.pro.eps, *ang, a.pro.k_out + head0 * D, acc);
-        mean_finish<QE, D>(acc, nrows, 1.f, part, a.kbar + mrow, a.kbar16 + ((size_t)bh * a.Nbp + J) * D);
+        mean_finish<QE, D>(acc, nrows, 1.f, part, a.kbar + mrow, a.kbar16 + ((size_t)bh * a.Nbp + J) * D,
+                           (size_t)a.BH * a.Nbp * D);
         if (tm.on) {
           // 3-D tile order: K also in position order
           const int c = threadIdx.x % TQ::CPR, g = threadIdx.x / TQ::CPR;
@@ -291,7 +299,7 @@ __device__ __forceinline__ void pool_block(const PoolArgs& a, int J, int bh, flo
       }
       block_mean<QE, D>(rq, nrows, qm, part, a.qbar + mrow, nullptr);
       uint16_t* k16 = (VE == ELT_BF16) ? a.kbar16 + ((size_t)bh * a.Nbp + J) * D : nullptr;
-      block_mean<QE, D>(rk, nrows, km, part, a.kbar + mrow, k16);
+      block_mean<QE, D>(rk, nrows, km, part, a.kbar + mrow, k16, (size_t)a.BH * a.Nbp * D);
     }
   };
 
@@ -336,6 +344,7 @@ __device__ __forceinline__ void pool_block(const PoolArgs& a, int J, int bh, flo
             if (threadIdx.x < D) {
               const int d = threadIdx.x;
               a.kbar16[((size_t)bh * a.Nbp + JJ) * D + d] = 0;
+              a.kbar16[((size_t)(a.BH + bh) * a.Nbp + JJ) * D + d] = 0;
               const size_t grp = (size_t)bh * (a.Nbp / 64) + (JJ >> 6);
               a.vbarT16[(grp * D + d) * 64 + (JJ & 63)] = 0;
             }

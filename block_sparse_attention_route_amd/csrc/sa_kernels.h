@@ -83,7 +83,8 @@ struct AttnArgs {
   const float* qbar;
   const float* kbar;
   const float* vbar;
-  const uint16_t* kbar16;
+  const uint16_t* kbar16;    // bf16(kbar) [BH][Nbp][D]
+  const uint16_t* kbarlo16;  // bf16(kbar - bf16(kbar)) [BH][Nbp][D]
   const uint16_t* vbarT16;
   const uint16_t* vt16;
   TileMap tm;            // position -> token order (on == 0: raster)

@@ -4,7 +4,8 @@
 //   qbar    float [BH][Nb][D]         block means of Q (fp8: dequantised)
 //   kbar    float [BH][Nb][D]         block means of K
 //   vbar    float [BH][Nb][D]         block means of V
-//   kbar16  bf16  [BH][Nbp][D]        bf16(kbar), rows >= Nb zero       (bf16 V only)
+//   kbar16  bf16  [2][BH][Nbp][D]     kbar in two bf16 halves: [0] = bf16(kbar),
+//                                     [1] = bf16(kbar - [0]); rows >= Nb zero (bf16 V only)
 //   vbarT16 bf16  [BH][Nbp/64][D][64] bf16(vbar) grouped 64 blocks at a
 //                                     time and transposed, cols >= Nb zero (bf16 V only)
 //   vt16    bf16  [BH][Nb][D][64]     V regrouped per 64-key block and
@@ -13,10 +14,11 @@
 //                                     3-D tile order (bf16 K only)
 //   sched   int   [64]                group counters of the sparse attention
 //                                     kernel's persistent workgroups
-//   vprime  bf16  [BH][Nb][Nbp][D]    first-order values of the skipped blocks,
-//                                     per query block I and key block J, rows
-//                                     J >= Nb zero; only with correction mode 2
-//                                     (fp32 inputs: float [BH][Nb][Nb][D])
+//   vprime  bf16  [S][Nb][Nbp][D]     first-order values of the skipped blocks
+//                                     of a slab of S heads, per query block I
+//                                     and key block J, rows J >= Nb zero; only
+//                                     with correction mode 2 (fp32 inputs:
+//                                     float [S][Nb][Nb][D]).  S = first_order_slab()
 //
 // The dense path uses only vt16.  Blocks are formed over positions: position
 // i is token i in the raster order, or token_of(i) in the 3-D tile order.
@@ -96,6 +98,24 @@ __host__ __device__ inline int token_of(const TileMap& m, int pos) {
 
 __host__ __device__ inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+// The first-order values are computed and consumed a slab of heads at a
+// time: as many heads as fit in kFirstOrderSlabBytes (at least one head, at
+// most all of them).
+constexpr size_t kFirstOrderSlabBytes = (size_t)4 << 30;
+
+__host__ __device__ inline size_t first_order_head_bytes(int64_t N, int64_t D, bool v_bf16) {
+  const int64_t Nb = (N + kBlock - 1) / kBlock;
+  const int64_t Nbp = (Nb + 63) / 64 * 64;
+  return v_bf16 ? (size_t)(Nb * Nbp * D) * 2 : (size_t)(Nb * Nb * D) * 4;
+}
+
+__host__ __device__ inline int64_t first_order_slab(int64_t BH, int64_t N, int64_t D, bool v_bf16) {
+  const size_t per = first_order_head_bytes(N, D, v_bf16);
+  int64_t s = per > 0 ? (int64_t)(kFirstOrderSlabBytes / per) : BH;
+  if (s < 1) s = 1;
+  return s < BH ? s : BH;
+}
+
 __host__ __device__ inline WsLayout ws_layout(int64_t BH, int64_t N, int64_t D, bool v_bf16,
                                               bool dense_only, bool tiled = false, bool first_order = false) {
   const int64_t Nb = (N + kBlock - 1) / kBlock;
@@ -112,7 +132,7 @@ __host__ __device__ inline WsLayout ws_layout(int64_t BH, int64_t N, int64_t D, 
     L.kbar = take((size_t)(BH * Nb * D) * 4);
     L.vbar = take((size_t)(BH * Nb * D) * 4);
     if (v_bf16) {
-      L.kbar16 = take((size_t)(BH * Nbp * D) * 2);
+      L.kbar16 = take((size_t)(2 * BH * Nbp * D) * 2);
       L.vbarT16 = take((size_t)(BH * Nbp * D) * 2);
     }
   }
@@ -120,7 +140,7 @@ __host__ __device__ inline WsLayout ws_layout(int64_t BH, int64_t N, int64_t D, 
   if (tiled && v_bf16 && !dense_only) L.kpos16 = take((size_t)(BH * N * D) * 2);
   if (!dense_only) L.sched = take(256);
   if (first_order && !dense_only)
-    L.vprime = v_bf16 ? take((size_t)BH * Nb * Nbp * D * 2) : take((size_t)BH * Nb * Nb * D * 4);
+    L.vprime = take((size_t)first_order_slab(BH, N, D, v_bf16) * first_order_head_bytes(N, D, v_bf16));
   L.total = off;
   return L;
 }

@@ -56,7 +56,7 @@
 extern "C" {
 #endif
 
-#define SA_ABI_VERSION 3
+#define SA_ABI_VERSION 4
 #define SA_BLOCK 64
 #define SA_MAX_NB 4096
 #define SA_MAX_N (SA_BLOCK * SA_MAX_NB)
@@ -100,9 +100,12 @@ typedef struct sa_shape {
  * in the key's deviation d_j = k_j - kbar_J, coefficient taken at the query
  * block mean: a skipped block keeps the weight n_J exp(s q_i . kbar_J) and
  * takes the value vbar_J + (s / n_J) sum_j (qbar_I . d_j) v_j (fp8 keys:
- * dequantised).  The pool step then also writes these values, one D-vector
- * per (query block, key block), and the workspace grows by B*H*Nb*Nbp*D bf16
- * (Nbp = Nb rounded up to 64), or B*H*Nb*Nb*D fp32 for fp32 inputs.
+ * dequantised).  The attention call (sa_forward, sa_forward_pooled) computes
+ * these values, one D-vector per (query block, key block), for a slab of
+ * heads at a time right before the attention over that slab, with this
+ * params' scale; the workspace grows by one slab of values (see
+ * sa_first_order_slab_heads: at most 4 GiB, or one head where a head needs
+ * more).  Every dtype pair supports it.
  * scale: softmax scale s; <= 0 selects 1/sqrt(D); must be finite.
  * topk: 0 = threshold routing with tau; > 0 = fixed budget instead: every
  * query block keeps the min(topk, Nb) key blocks of largest proxy, equal
@@ -164,16 +167,18 @@ const char* sa_last_error(void);
 sa_status sa_last_status(void);
 
 /* Workspace bytes that sa_pool / sa_route / sa_forward / sa_forward_pooled
- * need for this shape and dtypes (block means in fp32, bf16 copies of the
- * key/value means, and V regrouped per 64-key block).  Returns 0 if the
- * arguments are invalid.  Pass params = NULL for the default params. */
+ * need for this shape, dtypes and params (block means in fp32; for bf16 V the
+ * key means in two bf16 halves, the bf16 value means and V regrouped per
+ * 64-key block; 256 bytes of counters of the attention kernel's workgroup
+ * schedule; K in tile order with a 3-D tile order; one slab of first-order
+ * values with correction == 2).  Returns 0 if the arguments are invalid.
+ * Pass params = NULL for the default params. */
 size_t sa_workspace_bytes(const sa_shape* shape, const sa_params* params, const sa_inputs* in);
 
 /* Step "pool" (the pooled score's operands): writes qbar, kbar, vbar (fp32
  * means over each block's actual n_J tokens; fp8 inputs are dequantised with
- * their block scale) and the regrouped V used by the attention kernels into
- * the workspace; with params->correction == 2 also the first-order values of
- * every (query block, key block) pair. */
+ * their block scale), the bf16 copies of the means and the regrouped V used
+ * by the attention kernels into the workspace. */
 sa_status sa_pool(const sa_shape* shape, const sa_params* params, const sa_inputs* in,
                   void* ws, size_t ws_bytes, void* stream);
 
@@ -216,12 +221,31 @@ sa_status sa_forward_pooled(const sa_shape* shape, const sa_params* params, cons
  * The workspace then holds exactly what sa_pool would compute from q_out,
  * k_out and v (block means over the blocks that params selects, the bf16
  * copies, V regrouped, K in tile order), so sa_forward_pooled with inputs
- * {q_out, k_out, v} completes the attention.  params is used for its block
- * order and workspace layout only.  Only bf16 Q/K/V (SA_ERR_UNSUPPORTED
- * otherwise); gains 4-byte aligned, outputs 16-byte aligned. */
+ * {q_out, k_out, v} and the same params completes the attention (with
+ * correction == 2 that call also computes the first-order values, from the
+ * produced Q/K and its own scale).  params is used for its block order and
+ * workspace layout only.  Only bf16 Q/K/V (SA_ERR_UNSUPPORTED otherwise);
+ * gains 4-byte aligned, outputs 16-byte aligned. */
 sa_status sa_qk_prologue(const sa_shape* shape, const sa_params* params, const sa_prologue* pro,
                          const sa_inputs* in, const float* q_gain, const float* k_gain, void* q_out,
                          void* k_out, void* ws, size_t ws_bytes, void* stream);
+
+/* Heads per slab of the first-order correction (params->correction == 2):
+ * sa_forward / sa_forward_pooled compute the first-order values of this many
+ * heads at a time, each slab right before the attention over it, and the
+ * workspace holds one slab: min(B*H, max(1, floor(4 GiB / per-head bytes))),
+ * with Nb*Nbp*D bf16 values per head (Nb*Nb*D fp32 for fp32 inputs).  This
+ * bounds the first-order workspace at 4 GiB, or one head where a head needs
+ * more.  Returns 0 on invalid arguments or B*H*N == 0. */
+int64_t sa_first_order_slab_heads(const sa_shape* shape, const sa_inputs* in);
+
+/* Fixed budget for a sparsity f (the fraction of the Nb = ceil(N / 64) key
+ * blocks a query block skips; PISA runs at a fixed sparsity, paper review of
+ * the Sol Video Inference Engine, xllm-io blog): topk = ceil((1 - f) * Nb),
+ * at least 1 and at most Nb, for sa_params.topk.  A product within 1e-9 of
+ * an integer counts as that integer.  Returns 0 (SA_ERR_PARAM in
+ * sa_last_status) unless N >= 1 and 0 <= f < 1. */
+int32_t sa_budget_blocks(int32_t N, double sparsity);
 
 /* Workspace bytes for sa_dense_forward (0 on invalid arguments). */
 size_t sa_dense_workspace_bytes(const sa_shape* shape, const sa_inputs* in);

@@ -10,9 +10,8 @@ Tolerances (fixed by the method's stated bars):
 * masks: bit-exact except blocks whose float64 proxy lies within 1e-3 of the
   threshold (those are counted); outputs are then compared with the oracle
   evaluated on the GPU's mask.
-LSE of the bf16/fp8 paths has no stated bar; the bound used (2e-2 absolute)
-is derived next to TOL below from the bf16 rounding of P and of the
-correction operands.
+LSE of the bf16/fp8 paths has no stated bar; the bound used (1e-2 absolute)
+is derived next to TOL below from the bf16 rounding of P.
 """
 from __future__ import annotations
 
@@ -27,15 +26,16 @@ from oracle import attention as orc
 BAND = 1e-3
 # O tolerances are the stated bars (fp32: row-normwise relative 1e-5; bf16: max
 # abs 2e-2, mean abs 2e-3; fp8: max abs 4e-2).  LSE has no stated bar; ours is
-# derived from the arithmetic: the bf16 paths round P to bf16 (relative 2^-9
-# per weight) and the correction operands kbar, vbar to bf16, so a correction
-# logit s*q.kbar carries up to 2^-9 * s*|q||kbar|, about 1e-2 at the logit
-# scale of these workloads, and it enters the LSE with the (dominant, when few
-# blocks are kept) weight of the skipped blocks: 2e-2 for bf16 and fp8.
+# derived from the arithmetic: every logit is exact up to float32 rounding
+# (bf16 or fp8 products accumulated in float32; the correction logits take
+# the key means in two bf16 halves, about 16 significant bits, so
+# s*q.kbar is off by about 2^-17 of s*|q||kbar|), and the row sum is taken
+# over weights rounded to bf16 (relative 2^-8 at most each), so the LSE is off
+# by at most about 2^-8 = 4e-3: 1e-2 for bf16 and fp8.
 TOL = {
     "f32": dict(row_rel=1e-5, lse_rel=1e-5),
-    "bf16": dict(max_abs=2e-2, mean_abs=2e-3, lse_abs=2e-2),
-    "fp8": dict(max_abs=4e-2, lse_abs=2e-2),
+    "bf16": dict(max_abs=2e-2, mean_abs=2e-3, lse_abs=1e-2),
+    "fp8": dict(max_abs=4e-2, lse_abs=1e-2),
 }
 
 
@@ -101,11 +101,8 @@ def mask_check_topk(inp, b, h, gpu_mask: np.ndarray, topk: int, scale=None, orde
 
 
 def output_check(inp, b, h, o_gpu: torch.Tensor, lse_gpu: torch.Tensor, keep: np.ndarray, tau: float,
-                 correction: bool, qblocks=None, scale=None, dense=False, order=None, lse_abs=None):
+                 correction: bool, qblocks=None, scale=None, dense=False, order=None):
     """Oracle output for the given query blocks of head (b, h) against the GPU's.
-
-    lse_abs: the LSE bound when the case's logit scale is far from the
-    workloads' (the bf16 bound below is derived at their scale).
 
     order: position -> token map (3-D tile order); qblocks and keep then index
     blocks of positions, and the rows compared are the tokens they hold."""
@@ -139,5 +136,5 @@ def output_check(inp, b, h, o_gpu: torch.Tensor, lse_gpu: torch.Tensor, keep: np
         assert stats["max_abs"] <= t["max_abs"], stats
         if "mean_abs" in t:
             assert stats["mean_abs"] <= t["mean_abs"], stats
-        assert stats["lse_abs"] <= (t["lse_abs"] if lse_abs is None else lse_abs), stats
+        assert stats["lse_abs"] <= t["lse_abs"], stats
     return stats

@@ -35,7 +35,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_abi_version(lib):
-    assert api.sa_abi_version() == 3
+    assert api.sa_abi_version() == 4
 
 
 def test_status_strings(lib):
@@ -67,8 +67,9 @@ def test_workspace_bytes_layout(lib):
 
     def a256(x):
         return (x + 255) // 256 * 256
-    # means, bf16 mean copies, V regrouped, 256 bytes of group counters
-    expect = 3 * a256(BH * Nb * D * 4) + 2 * a256(BH * Nbp * D * 2) + a256(BH * Nb * D * 64 * 2) + 256
+    # means, bf16 key means (two halves) and value means, V regrouped, 256 bytes of group counters
+    expect = (3 * a256(BH * Nb * D * 4) + a256(2 * BH * Nbp * D * 2) + a256(BH * Nbp * D * 2)
+              + a256(BH * Nb * D * 64 * 2) + 256)
     assert n == expect
     # fp32 path keeps only the fp32 means (and the counters)
     n32 = lib.sa_workspace_bytes(ctypes.byref(sh), None, ctypes.byref(_inputs(api.SA_F32, api.SA_F32)))
@@ -229,6 +230,30 @@ def test_budget_blocks(sparsity, N, expect):
 def test_budget_blocks_rejects_out_of_range(sparsity):
     with pytest.raises(ValueError):
         api.budget_blocks(sparsity, 640)
+
+
+def test_budget_blocks_c_abi(lib):
+    assert lib.sa_budget_blocks(75600, 0.8) == 237      # ceil(236.4)
+    assert lib.sa_budget_blocks(6400, 0.9) == 10        # (1 - 0.9) * 100 is 10 up to rounding
+    assert lib.sa_budget_blocks(0, 0.5) == 0
+    assert api.status_name(lib.sa_last_status()) == "SA_ERR_PARAM"
+    assert lib.sa_budget_blocks(64, math.nan) == 0
+
+
+def test_first_order_slab_bounds_the_workspace(lib):
+    # per head: Nb * Nbp * D bf16 values; a slab holds floor(4 GiB / that) heads
+    def slab(H, N, D, dt=api.SA_BF16):
+        sh = _shape(B=1, H=H, T=1, Hg=1, Wg=N, D=D)
+        return lib.sa_first_order_slab_heads(ctypes.byref(sh), ctypes.byref(_inputs(dt, dt)))
+    assert slab(40, 75600, 128) == 11          # 1182 * 1216 * 128 * 2 B = 368 MB per head
+    assert slab(32, 171360, 128) == 2          # 1.84 GB per head
+    assert slab(3, 262144, 128) == 1           # exactly 4 GiB per head
+    assert slab(2, 1024, 64) == 2              # everything fits
+    assert slab(2, 1024, 64, api.SA_F32) == 2
+    sh = _shape(B=1, H=40, T=1, Hg=1, Wg=75600, D=128)
+    base = lib.sa_workspace_bytes(ctypes.byref(sh), ctypes.byref(_params(corr=1)), ctypes.byref(_inputs()))
+    fo = lib.sa_workspace_bytes(ctypes.byref(sh), ctypes.byref(_params(corr=2)), ctypes.byref(_inputs()))
+    assert fo - base == 11 * 1182 * 1216 * 128 * 2
 
 
 def test_last_status_explains_a_zero_size(lib):

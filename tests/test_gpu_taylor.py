@@ -6,8 +6,9 @@ oracle.
   above one, explicit scale, bf16, float32 and fp8 Q/K inputs: masks and
   every row's O and LSE against the oracle's first-order model (float32 at
   its 1e-5 bounds, fp8 at its 4e-2 bound);
-* the first-order values themselves (the section sa_pool appends to the
-  workspace) against oracle.first_order_value for every (query block, key
+* the first-order values themselves (the workspace section the attention
+  call fills, one slab of heads at a time; at these sizes one slab holds
+  every head) against oracle.first_order_value for every (query block, key
   block) pair of a case, padding rows zero;
 * LSE against the mean copies' run on the same inputs: the first-order model
   changes the skipped blocks' values only, and the kernel takes the same
@@ -16,9 +17,11 @@ oracle.
 * the fused producer step followed by the first-order path;
 * the maximum sequence length (N = 262,144, Nb = 4096);
 * the 720p size (B = 1, H = 40, 21 x 45 x 80, bf16) at tau = 2, the
-  configuration the benchmark times for this mode: masks of every head, O
-  and LSE of sampled query blocks of four heads; and the 720p CFG fp8
-  configuration (B = 2) at tau = 4, two heads.
+  configuration the benchmark times for this mode (4 slabs of at most 11
+  heads): masks of every head, O and LSE of sampled query blocks of four
+  heads; the 720p CFG fp8 configuration (B = 2) at tau = 4, two heads; and
+  the 1080p configuration (B = 1, H = 32, 21 x 68 x 120, tau = 4; 16 slabs
+  of 2 heads), four heads from different slabs.
 """
 import math
 
@@ -191,9 +194,11 @@ def test_keep_all_equals_mean_copies():
 
 
 def test_producer_then_first_order():
-    """sa_qk_prologue with correction 2 leaves the workspace sa_pool would
-    write from its outputs, first-order values included (the producer's own
-    parity is covered with the producer's tests)."""
+    """sa_qk_prologue leaves the workspace sa_pool would write from its
+    outputs (everything in front of the first-order values, which the
+    attention call computes), and the first-order attention on the two
+    workspaces agrees bit for bit (the producer's own parity is covered with
+    the producer's tests)."""
     B, H, grid, D = 1, 3, (3, 8, 12), 128
     N = grid[0] * grid[1] * grid[2]
     say(f"case producer B={B} H={H} grid={grid}")
@@ -208,7 +213,12 @@ def test_producer_then_first_order():
     qo, ko, ws = api.sa_qk_prologue(xq, xk, v, grid, qg, kg, tau=1.0, correction=2)
     ws2 = api.sa_pool(qo, ko, v, grid, tau=1.0, correction=2)
     torch.cuda.synchronize()
-    assert torch.equal(ws, ws2)
+    off = api.sa_workspace_bytes(qo, ko, v, grid, correction=1)
+    assert torch.equal(ws[:off], ws2[:off])
+    o1, l1, _ = api.sa_forward_pooled(qo, ko, v, grid, tau=1.0, correction=2, workspace=ws)
+    o2, l2, _ = api.sa_forward_pooled(qo, ko, v, grid, tau=1.0, correction=2, workspace=ws2)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
 
 
 def test_first_order_maximum_sequence_length():
@@ -292,3 +302,27 @@ def test_first_order_720p():
         qb = {0, wl.Nb - 1, int(rng.integers(wl.Nb)), int(rng.integers(wl.Nb))}
         st = output_check(inp, b, h, o, lse, keep, tau, 2, qblocks=qb)
         say(f"  head ({b},{h}) blocks {sorted(qb)}: {st}")
+
+
+def test_first_order_1080p():
+    """The 1080p configuration with the first-order correction: its values
+    take 1.84 GB per head, so the call runs 16 slabs of 2 heads.  Kept counts
+    of every head against sa_route; masks and sampled query blocks of heads
+    from the first, a middle and the last slab against the oracle."""
+    wl = synth.workload("1080p")
+    tau = wl.taus[0]
+    say(f"case 1080p first-order tau={tau}")
+    inp = synth.generate(wl)
+    q, k, v, _, _ = to_gpu(inp)
+    assert api.first_order_slab(q, v) == 2
+    grid = (wl.T, wl.Hg, wl.Wg)
+    ws = api.sa_pool(q, k, v, grid, tau=tau, correction=2)
+    o, lse, kept = api.sa_forward_pooled(q, k, v, grid, tau=tau, correction=2, workspace=ws, want_kept=True)
+    mask, kept_r = api.sa_route(q, k, v, grid, tau=tau)
+    torch.cuda.synchronize()
+    assert torch.equal(kept.cpu(), kept_r.cpu())
+    del ws, q, k, v
+    for (b, h) in [(0, 0), (0, 1), (0, 17), (0, wl.H - 1)]:
+        keep, _, _ = mask_check(inp, b, h, mask[b, h].cpu().numpy(), tau)
+        st = output_check(inp, b, h, o, lse, keep, tau, 2, qblocks=[0, 1339, wl.Nb - 1])
+        say(f"  head ({b},{h}): {st}")
