@@ -17,7 +17,7 @@ import torch
 __all__ = [
     "SaError", "load_library", "library_path", "Shape", "Params", "Inputs",
     "sa_abi_version", "sa_workspace_bytes", "sa_dense_workspace_bytes", "sa_pool", "sa_route",
-    "sa_forward", "sa_forward_pooled", "sa_dense_forward", "sa_qk_prologue", "status_name",
+    "sa_forward", "sa_forward_noalloc", "sa_forward_pooled", "sa_dense_forward", "sa_qk_prologue", "status_name",
     "Prologue", "make_params", "budget_blocks", "first_order_slab",
     "SA_F32", "SA_BF16", "SA_FP8_E4M3", "BLOCK", "MAX_NB", "MAX_N",
 ]
@@ -105,6 +105,8 @@ def load_library():
     for fn in (lib.sa_forward, lib.sa_forward_pooled):
         fn.restype = st
         fn.argtypes = [P, S, I, vp, vp, vp, vp, sz, vp]
+    lib.sa_forward_noalloc.restype = st
+    lib.sa_forward_noalloc.argtypes = [P, S, I, vp, vp, vp, vp]
     lib.sa_qk_prologue.restype = st
     lib.sa_qk_prologue.argtypes = [P, S, ctypes.POINTER(Prologue), I, vp, vp, vp, vp, vp, sz, vp]
     lib.sa_dense_forward.restype = st
@@ -262,6 +264,20 @@ def sa_forward(q, k, v, grid, *, tau: float = math.inf, correction=True, scale: 
     sh, pr, inp = make_shape(q, grid), make_params(tau, correction, scale, topk, tile), make_inputs(q, k, v, q_scale, k_scale)
     _check(lib.sa_forward(ctypes.byref(sh), ctypes.byref(pr), ctypes.byref(inp), _ptr(out), _ptr(lse),
                           _ptr(kept), _ptr(ws), ws.numel(), _stream(q)))
+    return out, lse, kept
+
+
+def sa_forward_noalloc(q, k, v, grid, *, tau: float = math.inf, correction=True, scale: float = 0.0,
+                       q_scale=None, k_scale=None, out=None, lse=None, want_kept=False, kept=None,
+                       topk: int = 0, tile=None):
+    """sa_forward with the library's static scratch as the workspace (no
+    device allocation by the library; outputs are allocated here when not
+    given).  Returns (o, lse, kept or None)."""
+    lib = load_library()
+    out, lse, kept = _outs(q, v, out, lse, want_kept, kept)
+    sh, pr, inp = make_shape(q, grid), make_params(tau, correction, scale, topk, tile), make_inputs(q, k, v, q_scale, k_scale)
+    _check(lib.sa_forward_noalloc(ctypes.byref(sh), ctypes.byref(pr), ctypes.byref(inp), _ptr(out), _ptr(lse),
+                                  _ptr(kept), _stream(q)))
     return out, lse, kept
 
 

@@ -9,6 +9,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 
 #include "sa_kernels.h"
 #include "sa_layout.h"
@@ -324,6 +325,56 @@ sa_status run_attn(const Req& r, const sa_inputs* in, void* o, float* lse, int32
 }
 
 }  // namespace
+
+// ---------------------------------------------------------------------------
+// sa_forward_noalloc: sa_forward with the workspace in a static device array,
+// for callers that cannot allocate.  Each device holds its own copy of the
+// array; its device address is looked up once per device and kept.
+static __device__ __align__(256) uint8_t scratch[SA_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+sa_status scratch_for_current_device(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(SA_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return fail(SA_ERR_UNSUPPORTED, "device %d beyond %d devices", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr)
+      return fail(SA_ERR_HIP, "hipGetSymbolAddress(scratch): %s", hipGetErrorString(e));
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return SA_OK;
+}
+
+}  // namespace
+
+SA_API sa_status sa_forward_noalloc(const sa_shape* shape, const sa_params* params, const sa_inputs* in,
+                                    void* o, float* lse, int32_t* kept, void* stream) {
+  Req r{};
+  sa_status s;
+  if ((s = check_shape_inputs(shape, in, &r, false)) != SA_OK) return s;
+  if ((s = check_params(params, &r)) != SA_OK) return s;
+  if (r.empty) return ok();
+  if ((s = check_out(o, lse, kept)) != SA_OK) return s;
+  if (r.ws.total > (size_t)SA_NOALLOC_SCRATCH_BYTES)
+    return fail(SA_ERR_WORKSPACE, "sa_forward_noalloc: this call needs a %zu-byte workspace, above the %zu-byte "
+                "static scratch (SA_NOALLOC_SCRATCH_BYTES); use sa_forward with a caller workspace",
+                r.ws.total, (size_t)SA_NOALLOC_SCRATCH_BYTES);
+  void* ws = nullptr;
+  if ((s = scratch_for_current_device(&ws)) != SA_OK) return s;
+  hipStream_t st = (hipStream_t)stream;
+  if ((s = run_pool(r, in, ws, st)) != SA_OK) return s;
+  return run_attn(r, in, o, lse, kept, ws, true, st);
+}
 
 SA_API int32_t sa_abi_version(void) { return SA_ABI_VERSION; }
 

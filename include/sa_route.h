@@ -199,6 +199,23 @@ sa_status sa_route(const sa_shape* shape, const sa_params* params, const sa_inpu
 sa_status sa_forward(const sa_shape* shape, const sa_params* params, const sa_inputs* in,
                      void* o, float* lse, int32_t* kept, void* ws, size_t ws_bytes, void* stream);
 
+/* sa_forward for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same pool and attention kernels, with the workspace in a static device
+ * array of SA_NOALLOC_SCRATCH_BYTES (256 MiB) inside the library instead of
+ * a caller buffer.  Each GPU the library runs on holds its own array until
+ * the process ends; its address is looked up on the first call on a device.
+ * The call allocates nothing (no hipMalloc, hipFree or allocating library
+ * routine).  The caller still passes the inputs and outputs, as for
+ * sa_forward.  A call whose workspace (sa_workspace_bytes) exceeds the array
+ * returns SA_ERR_WORKSPACE and enqueues nothing.  Every call on a GPU shares
+ * that GPU's array and leaves its contents behind; each call rewrites all it
+ * reads.  Calls that overlap on one GPU (different streams or threads
+ * without ordering between them) race on the array: serialise them. */
+#define SA_NOALLOC_SCRATCH_BYTES (256u << 20)
+sa_status sa_forward_noalloc(const sa_shape* shape, const sa_params* params, const sa_inputs* in,
+                             void* o, float* lse, int32_t* kept, void* stream);
+
 /* sa_forward without the pool step: the workspace must already hold the
  * output of sa_pool for the same inputs, shape and params. */
 sa_status sa_forward_pooled(const sa_shape* shape, const sa_params* params, const sa_inputs* in,

@@ -256,6 +256,18 @@ def test_first_order_slab_bounds_the_workspace(lib):
     assert fo - base == 11 * 1182 * 1216 * 128 * 2
 
 
+def test_noalloc_rejects_a_workspace_above_its_scratch(lib):
+    # 720p: the workspace (about 0.85 GB) exceeds the 256 MiB static scratch;
+    # refused on the host, before any HIP call
+    sh = _shape(B=1, H=40, T=21, Hg=45, Wg=80, D=128)
+    st = lib.sa_forward_noalloc(ctypes.byref(sh), ctypes.byref(_params()), ctypes.byref(_inputs()),
+                                FAKE, FAKE, None, None)
+    assert api.status_name(st) == "SA_ERR_WORKSPACE"
+    assert b"SA_NOALLOC_SCRATCH_BYTES" in lib.sa_last_error()
+    n = lib.sa_workspace_bytes(ctypes.byref(sh), ctypes.byref(_params()), ctypes.byref(_inputs()))
+    assert n > 256 << 20
+
+
 def test_last_status_explains_a_zero_size(lib):
     sh = _shape()
     inp = _inputs(qk=api.SA_FP8_E4M3, v=api.SA_BF16)
