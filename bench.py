@@ -29,6 +29,10 @@ and 8, 480p, 1080p and the 720p CFG batch with fp8 Q/K, each with its dense
 call, density, and -- from the CPU leg -- the near-threshold and flipped
 block counts of every head.
 
+gemm_reference times a plain 16384^3 bf16 GEMM through torch.matmul (the
+vendor's GEMM library) in the same run: the matrix-core rate this GPU
+sustains for dense bf16 work, next to the published peak the roofline uses.
+
 Pool bandwidth is quoted on the pass's algorithmic bytes (Q, K and V read
 once plus the three float32 mean tensors written, and the fp8 block scales),
 with this library's own layout bytes (bf16 key/value means and V regrouped
@@ -231,6 +235,29 @@ def pool_layout_bytes(wl) -> int:
     return b
 
 
+def gemm_reference(dev, n: int = 16384, reps: int = 3) -> dict:
+    """A plain bf16 GEMM (n x n x n) through torch.matmul, i.e. the vendor's
+    tuned GEMM library: the matrix-core rate this GPU sustains for dense bf16
+    work in the same run.  Context for the roofline, whose peak is the
+    published one (2.5 PFLOP/s at the 2.4 GHz peak clock)."""
+    a = torch.randn(n, n, dtype=torch.bfloat16, device=dev)
+    b = torch.randn(n, n, dtype=torch.bfloat16, device=dev)
+    c = a @ b
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        c = a @ b
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    del a, b, c
+    torch.cuda.empty_cache()
+    tflops = 2.0 * n ** 3 / (ms * 1e-3) / 1e12
+    return {"what": f"torch.matmul bf16 {n}x{n}x{n}", "ms": ms, "tflops": tflops,
+            "frac_of_published_peak": tflops / PEAK_BF16_TFLOPS}
+
+
 def time_config(name, tau, steps, dense_steps, cpu, inp=None, dev=None):
     """One workload at one tau: sa_pool + sa_forward_pooled timed over `steps`
     calls after a warm-up call, the dense call, density and (cpu) the oracle's
@@ -322,6 +349,8 @@ def main() -> None:
     ap.add_argument("--configs", default="720p:4,720p:8,480p:4,1080p:4,720p_cfg_fp8:4",
                     help="other workloads to time as name:tau (comma list, '' for none)")
     ap.add_argument("--config-steps", type=int, default=3)
+    ap.add_argument("--no-gemm-reference", dest="gemm_reference", action="store_false",
+                    help="skip the bf16 library GEMM timed as the matrix-core reference")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run one 1 GiB device-to-device copy (reference for the PMC byte counters)")
     args = ap.parse_args()
@@ -596,6 +625,8 @@ def main() -> None:
         copy_ms = e0.elapsed_time(e1) / 5
     del src, dst
 
+    gemm_ref = gemm_reference(dev) if args.gemm_reference else None
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(inp, wl, tau, o, args.cpu_heads)
@@ -656,6 +687,7 @@ def main() -> None:
         "fused_producer": producer,
         "first_order": first_order,
         "configs": configs,
+        "gemm_reference": gemm_ref,
         "cpu_baseline": cpu,
         "kernel_src": kernel_source_hash(),
     }
