@@ -99,9 +99,10 @@ __host__ __device__ inline int token_of(const TileMap& m, int pos) {
 __host__ __device__ inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 // The first-order values are computed and consumed a slab of heads at a
-// time: as many heads as fit in kFirstOrderSlabBytes (at least one head, at
-// most all of them).
-constexpr size_t kFirstOrderSlabBytes = (size_t)4 << 30;
+// time: the fewest slabs of equal size (up to one head) whose values fit in
+// kFirstOrderSlabBytes each -- or one head per slab where one head needs
+// more.
+constexpr size_t kFirstOrderSlabBytes = (size_t)8 << 30;
 
 __host__ __device__ inline size_t first_order_head_bytes(int64_t N, int64_t D, bool v_bf16) {
   const int64_t Nb = (N + kBlock - 1) / kBlock;
@@ -110,10 +111,12 @@ __host__ __device__ inline size_t first_order_head_bytes(int64_t N, int64_t D, b
 }
 
 __host__ __device__ inline int64_t first_order_slab(int64_t BH, int64_t N, int64_t D, bool v_bf16) {
+  if (BH < 1) return 0;
   const size_t per = first_order_head_bytes(N, D, v_bf16);
-  int64_t s = per > 0 ? (int64_t)(kFirstOrderSlabBytes / per) : BH;
-  if (s < 1) s = 1;
-  return s < BH ? s : BH;
+  int64_t fit = per > 0 ? (int64_t)(kFirstOrderSlabBytes / per) : BH;
+  if (fit < 1) fit = 1;
+  const int64_t slabs = (BH + fit - 1) / fit;
+  return (BH + slabs - 1) / slabs;
 }
 
 __host__ __device__ inline WsLayout ws_layout(int64_t BH, int64_t N, int64_t D, bool v_bf16,

@@ -104,7 +104,7 @@ typedef struct sa_shape {
  * these values, one D-vector per (query block, key block), for a slab of
  * heads at a time right before the attention over that slab, with this
  * params' scale; the workspace grows by one slab of values (see
- * sa_first_order_slab_heads: at most 4 GiB, or one head where a head needs
+ * sa_first_order_slab_heads: at most 8 GiB, or one head where a head needs
  * more).  Every dtype pair supports it.
  * scale: softmax scale s; <= 0 selects 1/sqrt(D); must be finite.
  * topk: 0 = threshold routing with tau; > 0 = fixed budget instead: every
@@ -250,10 +250,11 @@ sa_status sa_qk_prologue(const sa_shape* shape, const sa_params* params, const s
 /* Heads per slab of the first-order correction (params->correction == 2):
  * sa_forward / sa_forward_pooled compute the first-order values of this many
  * heads at a time, each slab right before the attention over it, and the
- * workspace holds one slab: min(B*H, max(1, floor(4 GiB / per-head bytes))),
- * with Nb*Nbp*D bf16 values per head (Nb*Nb*D fp32 for fp32 inputs).  This
- * bounds the first-order workspace at 4 GiB, or one head where a head needs
- * more.  Returns 0 on invalid arguments or B*H*N == 0. */
+ * workspace holds one slab.  The slabs are the fewest of equal size (up to
+ * one head) whose values fit in 8 GiB each, with Nb*Nbp*D bf16 values per
+ * head (Nb*Nb*D fp32 for fp32 inputs), or one head per slab where one head
+ * needs more.  This bounds the first-order workspace at 8 GiB, or one head.
+ * Returns 0 on invalid arguments or B*H == 0. */
 int64_t sa_first_order_slab_heads(const sa_shape* shape, const sa_inputs* in);
 
 /* Fixed budget for a sparsity f (the fraction of the Nb = ceil(N / 64) key

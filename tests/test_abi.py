@@ -241,19 +241,21 @@ def test_budget_blocks_c_abi(lib):
 
 
 def test_first_order_slab_bounds_the_workspace(lib):
-    # per head: Nb * Nbp * D bf16 values; a slab holds floor(4 GiB / that) heads
+    # per head: Nb * Nbp * D bf16 values; the fewest equal slabs of at most
+    # floor(8 GiB / that) heads each (at least one head per slab)
     def slab(H, N, D, dt=api.SA_BF16):
         sh = _shape(B=1, H=H, T=1, Hg=1, Wg=N, D=D)
         return lib.sa_first_order_slab_heads(ctypes.byref(sh), ctypes.byref(_inputs(dt, dt)))
-    assert slab(40, 75600, 128) == 11          # 1182 * 1216 * 128 * 2 B = 368 MB per head
-    assert slab(32, 171360, 128) == 2          # 1.84 GB per head
-    assert slab(3, 262144, 128) == 1           # exactly 4 GiB per head
+    assert slab(40, 75600, 128) == 20          # 368 MB per head: 23 fit, 2 slabs of 20
+    assert slab(32, 171360, 128) == 4          # 1.84 GB per head: 4 fit, 8 slabs of 4
+    assert slab(3, 262144, 128) == 2           # exactly 4 GiB per head: 2 fit
+    assert slab(5, 262144, 128) == 2           # 3 slabs: 2, 2, 1
     assert slab(2, 1024, 64) == 2              # everything fits
     assert slab(2, 1024, 64, api.SA_F32) == 2
     sh = _shape(B=1, H=40, T=1, Hg=1, Wg=75600, D=128)
     base = lib.sa_workspace_bytes(ctypes.byref(sh), ctypes.byref(_params(corr=1)), ctypes.byref(_inputs()))
     fo = lib.sa_workspace_bytes(ctypes.byref(sh), ctypes.byref(_params(corr=2)), ctypes.byref(_inputs()))
-    assert fo - base == 11 * 1182 * 1216 * 128 * 2
+    assert fo - base == 20 * 1182 * 1216 * 128 * 2
 
 
 def test_noalloc_rejects_a_workspace_above_its_scratch(lib):
