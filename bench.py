@@ -258,10 +258,12 @@ def gemm_reference(dev, n: int = 16384, reps: int = 3) -> dict:
             "frac_of_published_peak": tflops / PEAK_BF16_TFLOPS}
 
 
-def time_config(name, tau, steps, dense_steps, cpu, inp=None, dev=None):
+def time_config(name, tau, steps, dense_steps, cpu, inp=None, dev=None, first_order=False):
     """One workload at one tau: sa_pool + sa_forward_pooled timed over `steps`
     calls after a warm-up call, the dense call, density and (cpu) the oracle's
-    near-threshold / flipped counts over every head."""
+    near-threshold / flipped counts over every head; with first_order (bf16
+    only) also the call with the first-order correction (correction = 2),
+    whose values the attention call computes per slab of heads."""
     wl = synth.workload(name)
     t0 = time.time()
     if inp is None:
@@ -320,6 +322,30 @@ def time_config(name, tau, steps, dense_steps, cpu, inp=None, dev=None):
         rec["dense_tflops"] = f_dense / (dms * 1e-3) / 1e12
         rec["speedup_vs_dense"] = dms / ms
         del od, lsed, wsd
+    if first_order and wl.dtype == "bf16":
+        del ws
+        torch.cuda.empty_cache()
+        wsf = torch.empty(api.sa_workspace_bytes(q, k, v, grid, correction=2), dtype=torch.uint8, device=dev)
+
+        def fstep():
+            api.sa_pool(q, k, v, grid, tau=tau, correction=2, workspace=wsf)
+            api.sa_forward_pooled(q, k, v, grid, tau=tau, correction=2, workspace=wsf, out=o, lse=lse,
+                                  kept=kept, want_kept=True)
+        fstep()
+        torch.cuda.synchronize()
+        assert torch.equal(kept.cpu(), kept_r.cpu()), f"fused routing disagrees with sa_route ({name}, first order)"
+        e0.record()
+        for _ in range(steps):
+            fstep()
+        e1.record()
+        torch.cuda.synchronize()
+        fms = e0.elapsed_time(e1) / steps
+        per = api.first_order_slab(q, v)
+        rec["first_order"] = {"ms": fms, "time_vs_mean_copies": fms / ms, "heads_per_slab": per,
+                              "slabs": -(-(wl.B * wl.H) // per), "workspace_gib": wsf.numel() / 2 ** 30}
+        del wsf
+        ws = None
+        log(f"config {name} tau {tau:g}: first order {fms:.2f} ms ({fms / ms:.3f}x)")
     del q, k, v, ws, o, lse, kept
     torch.cuda.empty_cache()
     if cpu:
@@ -349,6 +375,8 @@ def main() -> None:
     ap.add_argument("--configs", default="720p:4,720p:8,480p:4,1080p:4,720p_cfg_fp8:4",
                     help="other workloads to time as name:tau (comma list, '' for none)")
     ap.add_argument("--config-steps", type=int, default=3)
+    ap.add_argument("--first-order-configs", default="1080p",
+                    help="workloads of --configs whose call with the first-order correction is timed too")
     ap.add_argument("--no-gemm-reference", dest="gemm_reference", action="store_false",
                     help="skip the bf16 library GEMM timed as the matrix-core reference")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -638,8 +666,9 @@ def main() -> None:
     for spec in [x for x in args.configs.split(",") if x.strip()]:
         cname, ctau = spec.split(":")
         same = cname == wl.name
+        fo_names = [x.strip() for x in args.first_order_configs.split(",") if x.strip()]
         configs.append(time_config(cname, float(ctau), args.config_steps, 1, not args.no_cpu_baseline,
-                                   inp=inp if same else None, dev=dev))
+                                   inp=inp if same else None, dev=dev, first_order=cname in fo_names))
 
     out = {
         "metric": METRIC,

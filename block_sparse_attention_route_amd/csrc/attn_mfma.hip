@@ -246,20 +246,24 @@ __global__ __launch_bounds__(128 * QB, QB == 2 ? 2 : 1) void attn_kernel(AttnArg
   constexpr int STAGE = C::KTILE + C::VTILE + ((SPARSE && !TAY) ? C::KTILE : 0);
   constexpr int LO_OFF = TAY ? C::KTILE : C::KTILE + C::VTILE;
   constexpr int SMEM_STAGE = ST * STAGE;
-  constexpr int SMEM_PROXY = SPARSE ? QB * kMaxNb * 4 : 0;
-  constexpr int SMEM = SMEM_STAGE > SMEM_PROXY ? SMEM_STAGE : SMEM_PROXY;
+  // The routing step's arrays (proxies, per-block flags, the fixed-budget
+  // histograms, the query means) are dead once the union list is built, and
+  // share the ring's LDS: the first tile is issued after that.
+  constexpr int R_FLAGS = QB * kMaxNb * 4, R_HIST = R_FLAGS + kMaxNb, R_QB = R_HIST + QB * 256 * 4;
+  constexpr int SMEM_ROUTE = SPARSE ? R_QB + QB * D * 4 : 0;
+  constexpr int SMEM = SMEM_STAGE > SMEM_ROUTE ? SMEM_STAGE : SMEM_ROUTE;
   static_assert(KI8 >= 1 && VI >= 1, "tile copies per wave");
   static_assert(!TAY || SPARSE, "first-order values: sparse only");
 
   __shared__ __attribute__((aligned(1024))) uint8_t smem[SMEM];
-  __shared__ uint8_t flags[SPARSE ? kMaxNb : 1];
+  uint8_t* const flags = smem + R_FLAGS;
+  int* const hist = reinterpret_cast<int*>(smem + R_HIST);
+  float* const qb = reinterpret_cast<float*>(smem + R_QB);
   __shared__ uint16_t ulist[SPARSE ? kMaxNb : 1];
   __shared__ uint64_t skipbits[SPARSE ? QB * (kMaxNb / 64) : 1];  // per query block, per 64-block chunk
-  __shared__ float qb[SPARSE ? QB * D : 1];
   __shared__ float redf[QB * NW];
   __shared__ int redi[QB * NW];
   __shared__ int counts[QB];
-  __shared__ int hist[SPARSE ? QB * 256 : 1];
   __shared__ uint32_t sel[SPARSE ? 3 * QB : 1];
   __shared__ int nunion_s;
   // correction mode 2: the first-order value tile of each query block, 64 key

@@ -389,7 +389,8 @@ __device__ __forceinline__ void topk_rows(const float* __restrict__ p, int Nb, i
 // Dense workgroups all cost the same and take chunks of about what an XCD
 // holds at once (SA_XCD_CHUNK); sparse ones differ in cost with the kept
 // density of their region, and smaller chunks (SA_XCD_CHUNK_SPARSE) spread
-// each region over the XCDs, which have no work stealing between them.
+// each region over the XCDs before an XCD that runs out of its own groups
+// takes those of the others.
 // CH = 0 keeps the plain order.  Tiles past the last whole round keep their
 // own index.
 template <int CH>
