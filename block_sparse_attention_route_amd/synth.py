@@ -108,13 +108,20 @@ class Inputs:
 
 
 def _field(rng: np.random.Generator, u: np.ndarray, D: int, ft_max: float) -> np.ndarray:
+    # Plain elementwise sums in a fixed order, no BLAS: heads are generated in
+    # parallel threads, and concurrent multi-threaded BLAS calls from several
+    # threads have returned wrong products with this numpy's OpenBLAS.
     N = u.shape[0]
     f = rng.uniform(0.0, 0.5, size=(4, 3))
     f[:, 0] = rng.uniform(0.0, ft_max, size=4)
     phi = rng.uniform(0.0, 2 * math.pi, size=4)
     a = rng.standard_normal(size=(4, D))
-    waves = np.sin(2 * math.pi * (u @ f.T) + phi[None, :])          # [N, 4]
-    x = (waves @ a).astype(np.float32)
+    arg = u[:, 0:1] * f[None, :, 0] + u[:, 1:2] * f[None, :, 1] + u[:, 2:3] * f[None, :, 2]   # [N, 4]
+    waves = np.sin(2 * math.pi * arg + phi[None, :])
+    x = waves[:, 0:1] * a[0]
+    for s in range(1, 4):
+        x += waves[:, s:s + 1] * a[s]
+    x = x.astype(np.float32)
     x += np.float32(0.3) * rng.standard_normal(size=(N, D), dtype=np.float32)
     return x
 

@@ -86,3 +86,13 @@ def test_fp8_zero_block_scale_is_one():
     codes, scale = synth._fp8_quantise(torch.zeros(70, 8), 64)
     assert torch.equal(scale, torch.ones(2))
     assert float(codes.to(torch.float32).abs().max()) == 0.0
+
+
+def test_deterministic_under_threads_at_full_length():
+    """Heads generated in parallel threads equal those generated one at a
+    time, at the 1080p sequence length (where a parallel BLAS product inside
+    the generator once gave thread-dependent results)."""
+    wl = synth.workload("1080p").with_(H=4)
+    a = synth.generate(wl, threads=4)
+    b = synth.generate(wl, threads=1)
+    assert torch.equal(a.q, b.q) and torch.equal(a.k, b.k) and torch.equal(a.v, b.v)
