@@ -184,6 +184,7 @@ def route_band_counts(inp, wl, tau, gpu_mask: np.ndarray) -> dict:
     Runs in the cpu_baseline leg (it is the oracle's routing)."""
     from oracle import attention as orc  # test infrastructure: cpu_baseline leg only
     from concurrent.futures import ThreadPoolExecutor
+    from threadpoolctl import threadpool_limits
 
     def one(bh):
         b, h = divmod(bh, wl.H)
@@ -194,7 +195,9 @@ def route_band_counts(inp, wl, tau, gpu_mask: np.ndarray) -> dict:
         return int(band.sum()), int((diff & band).sum()), int((diff & ~band).sum())
 
     t0 = time.perf_counter()
-    with ThreadPoolExecutor(max_workers=8) as ex:
+    # one BLAS thread per call: concurrent multi-threaded BLAS calls from
+    # several threads have returned wrong products with this numpy's OpenBLAS
+    with threadpool_limits(limits=1, user_api="blas"), ThreadPoolExecutor(max_workers=8) as ex:
         res = list(ex.map(one, range(wl.B * wl.H)))
     return {"heads": wl.B * wl.H, "near_threshold_blocks": sum(r[0] for r in res),
             "flipped_in_band": sum(r[1] for r in res), "differ_outside_band": sum(r[2] for r in res),

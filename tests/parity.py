@@ -44,6 +44,17 @@ def say(*a):
     sys.stdout.flush()
 
 
+def oracle_map(fn, items, workers: int = 8):
+    """fn over items in a thread pool, for oracle work on many heads.  BLAS
+    runs one thread per call meanwhile: concurrent multi-threaded BLAS calls
+    from several threads have returned wrong products with this numpy's
+    OpenBLAS."""
+    from concurrent.futures import ThreadPoolExecutor
+    from threadpoolctl import threadpool_limits
+    with threadpool_limits(limits=1, user_api="blas"), ThreadPoolExecutor(max_workers=workers) as ex:
+        return list(ex.map(fn, items))
+
+
 def to_gpu(inp):
     dev = torch.device("cuda:0")
     g = lambda t: None if t is None else t.to(dev).contiguous()  # noqa: E731

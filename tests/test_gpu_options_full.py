@@ -10,8 +10,6 @@ compared with the oracle on sampled tokens (grid corners and seeded random
 tokens, so the largest rotation angles are covered), its workspace bit for bit
 with sa_pool run on its own outputs.
 """
-from concurrent.futures import ThreadPoolExecutor
-
 import numpy as np
 import pytest
 import torch
@@ -19,7 +17,7 @@ import torch
 from block_sparse_attention_route_amd import api, synth
 from oracle import attention as orc
 from oracle import prologue as pro
-from tests.parity import mask_check, mask_check_topk, output_check, say, to_gpu
+from tests.parity import mask_check, mask_check_topk, oracle_map, output_check, say, to_gpu
 
 pytestmark = pytest.mark.gpu
 
@@ -45,8 +43,7 @@ def _sample(wl, rng):
 def _check_all(inp, mask_np, check, o, lse, tau, order=None, seed=7):
     wl = inp.wl
     heads = [(0, h) for h in range(wl.H)]
-    with ThreadPoolExecutor(max_workers=8) as ex:
-        res = list(ex.map(lambda bh: check(bh, mask_np[bh]), heads))
+    res = oracle_map(lambda bh: check(bh, mask_np[bh]), heads)
     say(f"  masks ok for {len(heads)} heads; density {mask_np.mean():.3f}; "
         f"near-threshold {sum(r[1] for r in res)}, flipped {sum(r[2] for r in res)}")
     rng = np.random.default_rng(seed)

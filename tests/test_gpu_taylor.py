@@ -31,7 +31,7 @@ import torch
 
 from block_sparse_attention_route_amd import api, synth
 from oracle import attention as orc
-from tests.parity import mask_check, mask_check_topk, output_check, say, to_gpu
+from tests.parity import mask_check, mask_check_topk, oracle_map, output_check, say, to_gpu
 
 pytestmark = pytest.mark.gpu
 
@@ -277,7 +277,6 @@ def test_first_order_720p_cfg_fp8():
 
 
 def test_first_order_720p():
-    from concurrent.futures import ThreadPoolExecutor
     wl, inp = _inputs_720p()
     tau = 2.0
     say(f"case 720p first-order tau={tau}")
@@ -292,8 +291,7 @@ def test_first_order_720p():
     mask_np = mask.cpu().numpy()
     del mask
     heads = [(0, h) for h in range(wl.H)]
-    with ThreadPoolExecutor(max_workers=8) as ex:
-        res = list(ex.map(lambda bh: mask_check(inp, bh[0], bh[1], mask_np[bh], tau), heads))
+    res = oracle_map(lambda bh: mask_check(inp, bh[0], bh[1], mask_np[bh], tau), heads)
     say(f"  masks ok for {len(heads)} heads; density {mask_np.mean():.3f}")
     rng = np.random.default_rng(11)
     sample = sorted({(0, 0), (0, wl.H - 1), (0, int(rng.integers(wl.H))), (0, int(rng.integers(wl.H)))})
