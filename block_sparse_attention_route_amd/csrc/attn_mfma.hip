@@ -32,7 +32,7 @@
 // Tiling.  A workgroup takes QB adjacent query blocks (QB = 4 at D = 128, 2
 // at D = 64) with two waves per block; wave w owns 32 query rows (query block
 // QB*group + w/2, rows 32*(w%2) ..) against the full 64-key tile.  Products
-// use v_mfma_f32_32x32x16_bf16 (v_mfma_f32_32x32x16_fp8_fp8 for fp8 Q K^T)
+// use v_mfma_f32_32x32x16_bf16 (v_mfma_f32_32x32x64_f8f6f4 for fp8 Q K^T)
 // with the roles transposed, S^T = K Q^T and O^T = V^T P^T: a lane owns one
 // query column, so the softmax row max and sum are lane-local plus one
 // exchange with lane^32, and the exponentiated scores are already the B
@@ -44,10 +44,13 @@
 // tile ahead, from a wave-uniform base address plus per-lane offsets computed
 // once, with an XOR swizzle on 16-byte chunks that keeps the MFMA operand
 // reads free of bank conflicts; the tile loop is unrolled by ring stage so
-// that the LDS operand addresses are immediates.  Workgroup ids are remapped so that
-// each XCD works on a chunk of adjacent query blocks while all XCDs stay on
-// the same head (shared key blocks hit in that XCD's L2, the head's K/V stays
-// in the last-level cache).
+// that the LDS operand addresses are immediates.  Work is ordered so that
+// each XCD takes chunks of adjacent query blocks while all XCDs stay on the
+// same head (shared key blocks hit in that XCD's L2, the head's K/V stays in
+// the last-level cache): the dense kernel remaps its workgroup ids; the
+// sparse kernel, whose groups differ in cost, runs one persistent workgroup
+// per CU that takes groups from its XCD's queue and, once that is empty,
+// from the other XCDs' queues.
 //
 // Softmax.  The running maximum is raised lazily and without a per-tile
 // maximum: the weights P = 2^(s - m) are taken against the maximum in use,
